@@ -1,0 +1,465 @@
+"""TileMix oracle -- a plain, slow, CPU-only statement of what the fused
+mixed-precision prefill path computes.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run this module.  It shares
+no code, tables or constants generator with the HIP library
+(``mixed_precision_attention_amd``) and never imports it; the only thing both
+sides consume in common is the seeded inputs drawn by ``synth``.
+
+Everything is numpy; floating point is float64 except where the method fixes a
+precision (the quantiser works in IEEE binary32, P is rounded to binary16
+before the P.V product).
+
+Sources (web pages about TileMix, cited by title and section):
+  [Digest]    "TileMix: Tile-Centric Mixed-Precision Attention for LLM Inference
+              Acceleration" -- paper digest page, method and setup paragraphs.
+  [Explainer] "TileMix：给AI大模型的“注意力”做一次精准的精度分配手术" -- popular
+              explainer, sections "第一步", "第二步", "第三步", "支持的场景".
+  [Routes]    "TileMix Routes Attention Precision at the Hardware-Tile Level",
+              section "Precision routing over score tiles".
+  [Map]       "Precision Has a Map: TileMix Routes INT8 Inside Dense Attention",
+              sections "Dense attention does not require uniform precision" and
+              "The routing mechanism is designed to stay inside the hot loop".
+
+Where the pages leave a step open, the reading taken is written next to the
+code that takes it.
+
+Parity pins: every function below is pinned by tests under ``tests/`` that do
+not retype its formula (hand-derived words, a published splitmix64 output,
+exact-rational quantisation, brute-force attention, closed forms).  Nothing
+here is "parity unpinned" except the routing templates' correspondence to the
+paper's own unpublished masks (the pages print no mask).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from fractions import Fraction
+
+import numpy as np
+
+# [Digest, method]: score tiles are BLOCK_M x BLOCK_N hardware tiles; the
+# quantisation blocks are 128 query rows and 64 key rows, so the score tiles
+# are read as 128 x 64 as well.
+BLOCK_M = 128
+BLOCK_N = 64
+# [Digest, method]: one 64-bit word per (KV head, query-tile row).
+WORD_BITS = 64
+
+TEMPLATES = ("band", "global", "rowrandom", "alignedsparse", "bigbird", "sptrans")
+
+_M64 = (1 << 64) - 1
+
+
+# ---------------------------------------------------------------------------
+# Geometry: tiles, groups, legal groups
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class SeqGeometry:
+    L: int          # sequence length
+    Tm: int         # query tiles (rows of the tile grid)
+    Tn: int         # key tiles
+    g: int          # grouping factor: key tiles per routing group
+    D: tuple        # D[r] = index of the last legal group of query-tile row r
+    last_tile: tuple  # last key tile holding a legal pair for row r
+
+    @property
+    def n(self):
+        """Legal groups per row."""
+        return tuple(d + 1 for d in self.D)
+
+    @property
+    def n_legal(self) -> int:
+        return sum(self.n)
+
+    def legal_groups(self):
+        """All legal (r, G), row-major."""
+        return [(r, G) for r in range(self.Tm) for G in range(self.D[r] + 1)]
+
+
+def seq_geometry(L: int) -> SeqGeometry:
+    """Tile grid of one causal sequence.
+
+    [Digest, method]: adjacent key tiles along the key dimension form a routing
+    group with one bit; the grouping factor g keeps the bits per row within 64.
+    Reading: g is the smallest integer that does so, g = ceil(Tn / 64) (at
+    least 1), and group G holds key tiles G*g .. G*g+g-1.  A group is legal for
+    row r when it holds at least one (query, key) pair with key <= query inside
+    the sequence ([Digest, method]: causal and boundary legality do not depend
+    on routing).
+    """
+    if L < 0:
+        raise ValueError("negative length")
+    Tm = -(-L // BLOCK_M)
+    Tn = -(-L // BLOCK_N)
+    g = max(1, -(-Tn // WORD_BITS))
+    D, last = [], []
+    for r in range(Tm):
+        last_q = min(BLOCK_M * r + BLOCK_M - 1, L - 1)
+        lt = last_q // BLOCK_N
+        last.append(lt)
+        D.append(lt // g)
+    return SeqGeometry(L, Tm, Tn, g, tuple(D), tuple(last))
+
+
+def int8_group_count(coverage_bp: int, n_legal: int) -> int:
+    """Number of INT8 groups for a coverage given in basis points.
+
+    [Digest, method]: coverage is the INT8 share of legal tile groups (not of
+    FLOPs).  Reading: rounded half up to a whole group, per sequence.
+    """
+    if not 0 <= coverage_bp <= 10000:
+        raise ValueError("coverage_bp must be in [0, 10000]")
+    return (coverage_bp * n_legal + 5000) // 10000
+
+
+# ---------------------------------------------------------------------------
+# Static templates.  [Digest, method]: routing is static and data-free; Band
+# keeps the diagonal-local part, Global keeps designated positions, Row-Random
+# keeps a random FP16 subset per row, Aligned-Sparse extends right-aligned,
+# BigBird is the union of the first three, SpTrans is stride plus tail.
+#
+# Reading: each template is a strict total order of a sequence's legal groups,
+# most-deserving-of-FP16 first; at a coverage the first N16 = N_legal - N8
+# groups stay FP16 and the rest go INT8.  With d = D(r) - G (distance in groups
+# from the row's diagonal group):
+#   band          (d, r, G)
+#   global        (G, r)                       designated positions = leading
+#                                              key groups (sink tokens)
+#   rowrandom     ((2*rho + 1) / (2*n_r), r, G), rho = rank of G in row r by
+#                                              (hash(r, G), G)
+#   alignedsparse ((2*d + 1) / (2*n_r), r, G)
+#   sptrans       union(stride, band), stride = (d mod s != 0, d, r, G) with
+#                                              s = max(1, isqrt(n of last row))
+#   bigbird       union(band, global, rowrandom)
+# union() is round-robin: each order in turn contributes its next group not yet
+# taken.
+# ---------------------------------------------------------------------------
+
+def splitmix64_mix(z: int) -> int:
+    """The splitmix64 output finaliser (Steele, Lea and Flood, "Fast splittable
+    pseudorandom number generators", 2014), on 64-bit unsigned integers."""
+    z &= _M64
+    z ^= z >> 30
+    z = (z * 0xBF58476D1CE4E5B9) & _M64
+    z ^= z >> 27
+    z = (z * 0x94D049BB133111EB) & _M64
+    z ^= z >> 31
+    return z
+
+
+def rowrandom_hash(seed: int, r: int, G: int) -> int:
+    """u(r, G) = mix(mix(seed) XOR (64 r + G)): keyed on the sequence-local row
+    and group only, so one template serves every batch entry and KV head."""
+    return splitmix64_mix(splitmix64_mix(seed) ^ (WORD_BITS * r + G))
+
+
+def _order_band(geo):
+    return sorted(geo.legal_groups(), key=lambda rg: (geo.D[rg[0]] - rg[1], rg[0], rg[1]))
+
+
+def _order_global(geo):
+    return sorted(geo.legal_groups(), key=lambda rg: (rg[1], rg[0]))
+
+
+def _order_rowrandom(geo, seed):
+    rank = {}
+    for r in range(geo.Tm):
+        gs = sorted(range(geo.D[r] + 1), key=lambda G: (rowrandom_hash(seed, r, G), G))
+        for rho, G in enumerate(gs):
+            rank[(r, G)] = rho
+    n = geo.n
+    return sorted(geo.legal_groups(),
+                  key=lambda rg: (Fraction(2 * rank[rg] + 1, 2 * n[rg[0]]), rg[0], rg[1]))
+
+
+def _order_alignedsparse(geo):
+    n = geo.n
+    return sorted(geo.legal_groups(),
+                  key=lambda rg: (Fraction(2 * (geo.D[rg[0]] - rg[1]) + 1, 2 * n[rg[0]]),
+                                  rg[0], rg[1]))
+
+
+def sptrans_stride(geo) -> int:
+    """Stride in groups of the SpTrans template: floor(sqrt(groups in the last
+    row)), at least 1 (the Sparse Transformer's strided pattern uses a stride
+    near the square root of the length)."""
+    if geo.Tm == 0:
+        return 1
+    return max(1, math.isqrt(geo.n[geo.Tm - 1]))
+
+
+def _order_sptrans(geo):
+    s = sptrans_stride(geo)
+    stride = sorted(geo.legal_groups(),
+                    key=lambda rg: (0 if (geo.D[rg[0]] - rg[1]) % s == 0 else 1,
+                                    geo.D[rg[0]] - rg[1], rg[0], rg[1]))
+    return union_orders(stride, _order_band(geo))
+
+
+def _order_bigbird(geo, seed):
+    return union_orders(_order_band(geo), _order_global(geo), _order_rowrandom(geo, seed))
+
+
+def union_orders(*orders):
+    """Round-robin union of several orders of the same set of groups."""
+    total = len(orders[0])
+    out, seen = [], set()
+    pos = [0] * len(orders)
+    while len(out) < total:
+        for i, o in enumerate(orders):
+            while pos[i] < len(o) and o[pos[i]] in seen:
+                pos[i] += 1
+            if pos[i] < len(o):
+                seen.add(o[pos[i]])
+                out.append(o[pos[i]])
+                pos[i] += 1
+                if len(out) == total:
+                    break
+    return out
+
+
+def template_order(geo: SeqGeometry, template: str, seed: int = 0):
+    """Legal groups of one sequence, most-deserving-of-FP16 first."""
+    if template == "band":
+        return _order_band(geo)
+    if template == "global":
+        return _order_global(geo)
+    if template == "rowrandom":
+        return _order_rowrandom(geo, seed)
+    if template == "alignedsparse":
+        return _order_alignedsparse(geo)
+    if template == "sptrans":
+        return _order_sptrans(geo)
+    if template == "bigbird":
+        return _order_bigbird(geo, seed)
+    raise ValueError(f"unknown template {template!r}")
+
+
+def int8_groups(geo: SeqGeometry, template: str, coverage_bp: int, seed: int = 0):
+    """Set of (r, G) routed to INT8 at a coverage: the tail of the order."""
+    order = template_order(geo, template, seed)
+    n8 = int8_group_count(coverage_bp, len(order))
+    return set(order[len(order) - n8:])
+
+
+def routing_words(seqlens, num_kv_heads: int, template: str, coverage_bp: int,
+                  seed: int = 0):
+    """Packed routing words for a varlen batch.
+
+    [Digest, method] / [Explainer, 第二步]: bit 1 selects INT8, bit 0 FP16; one
+    64-bit word per (KV head, query-tile row), looked up with a shift and a
+    mask.  Reading: bit G (least significant = group 0) belongs to group G;
+    bits of illegal groups are 0.  [Digest, method]: the same template is
+    reused across layers, batch entries and KV heads, so every KV head gets the
+    same words.
+
+    Returns (words uint64 [num_kv_heads, sum Tm], g int32 [B], int8 group count
+    int64 [B], legal group count int64 [B]).
+    """
+    geos = [seq_geometry(int(L)) for L in seqlens]
+    total_tm = sum(geo.Tm for geo in geos)
+    row_words = []
+    gs, n8s, nls = [], [], []
+    for geo in geos:
+        chosen = int8_groups(geo, template, coverage_bp, seed)
+        words = [0] * geo.Tm
+        for (r, G) in chosen:
+            words[r] |= 1 << G
+        row_words.extend(words)
+        gs.append(geo.g)
+        n8s.append(len(chosen))
+        nls.append(geo.n_legal)
+    out = np.zeros((num_kv_heads, total_tm), dtype=np.uint64)
+    out[:, :] = np.array(row_words, dtype=np.uint64)[None, :] if total_tm else 0
+    return (out, np.array(gs, dtype=np.int32), np.array(n8s, dtype=np.int64),
+            np.array(nls, dtype=np.int64))
+
+
+# ---------------------------------------------------------------------------
+# Blockwise symmetric quantiser
+# ---------------------------------------------------------------------------
+
+def quantize_blocks(x: np.ndarray, cu_seqlens, block: int):
+    """Blockwise symmetric INT8 quantisation of one operand.
+
+    [Digest, method]: only Q and K are quantised, in blocks of 128 x d (Q) and
+    64 x d (K), symmetric, scale = absmax / 127.  [Explainer, 第三步]: the
+    integer results are scaled back to floating point with the block scale.
+    Readings: one scale per (head, block) over that head's d channels; a block
+    at a sequence end holds only that sequence's rows; in binary32,
+    s = a / 127, q = round-half-even(x / s) clamped to [-127, 127]; an all-zero
+    block has s = 0 and q = 0.
+
+    x: float16 [T, H, d].  Returns (int8 [T, H, d], float32 scales [H, tiles])
+    with tiles numbered per sequence and concatenated over sequences.
+    """
+    cu = [int(c) for c in cu_seqlens]
+    T, H, d = x.shape
+    q = np.zeros((T, H, d), dtype=np.int8)
+    scales = []
+    for s in range(len(cu) - 1):
+        start, end = cu[s], cu[s + 1]
+        for b0 in range(start, end, block):
+            b1 = min(b0 + block, end)
+            blk = x[b0:b1].astype(np.float32)               # [rows, H, d]
+            a = np.abs(blk).max(axis=(0, 2))                  # [H], exact
+            sc = (a / np.float32(127.0)).astype(np.float32)   # binary32 division
+            qb = np.zeros(blk.shape, dtype=np.int8)
+            for h in range(H):
+                if a[h] == 0:
+                    continue
+                ratio = blk[:, h, :] / sc[h]                  # binary32 division
+                qb[:, h, :] = np.clip(np.rint(ratio), -127, 127).astype(np.int8)
+            q[b0:b1] = qb
+            scales.append(sc)
+    if scales:
+        sc_all = np.stack(scales, axis=1).astype(np.float32)  # [H, tiles]
+    else:
+        sc_all = np.zeros((H, 0), dtype=np.float32)
+    return q, sc_all
+
+
+# ---------------------------------------------------------------------------
+# Scores and attention
+# ---------------------------------------------------------------------------
+
+def _tile_offsets(seqlens):
+    qt, kt = [0], [0]
+    for L in seqlens:
+        geo = seq_geometry(int(L))
+        qt.append(qt[-1] + geo.Tm)
+        kt.append(kt[-1] + geo.Tn)
+    return qt, kt
+
+
+def softmax_scale(d: int) -> np.float32:
+    """1/sqrt(d) in binary32 ([Digest, method]: both paths restore the score
+    with 1/sqrt(d))."""
+    return np.float32(1.0 / math.sqrt(d))
+
+
+def int8_tile_scale(sq: np.float32, sk: np.float32, d: int) -> np.float32:
+    """Factor taking an INT8 tile's int32 accumulator to the common score
+    domain: fl32(fl32(s_q * s_k) * fl32(1/sqrt(d)))."""
+    return np.float32(np.float32(sq * sk) * softmax_scale(d))
+
+
+def qk_int32_tile(q_i8, k_i8, cu_seqlens, seq: int, head: int, r: int, t: int,
+                  hq: int, hkv: int) -> np.ndarray:
+    """int32 accumulator of one 128 x 64 score tile of the INT8 path: exact
+    integer dot products of int8 Q rows 128r.. and int8 K rows 64t.. over d
+    ([Digest, method]: INT8 MMA with INT32 accumulation).  Rows or columns
+    outside the sequence are 0."""
+    cu = [int(c) for c in cu_seqlens]
+    start, L = cu[seq], cu[seq + 1] - cu[seq]
+    kv = head // (hq // hkv)
+    out = np.zeros((BLOCK_M, BLOCK_N), dtype=np.int64)
+    q0, q1 = BLOCK_M * r, min(BLOCK_M * r + BLOCK_M, L)
+    k0, k1 = BLOCK_N * t, min(BLOCK_N * t + BLOCK_N, L)
+    if q1 > q0 and k1 > k0:
+        a = q_i8[start + q0:start + q1, head, :].astype(np.int64)
+        b = k_i8[start + k0:start + k1, kv, :].astype(np.int64)
+        out[:q1 - q0, :k1 - k0] = a @ b.T
+    return out.astype(np.int32)
+
+
+def prefill_attention(q, k, v, q_i8, k_i8, q_scale, k_scale, words, cu_seqlens,
+                      hq: int, hkv: int, rows=None, round_p: bool = True,
+                      return_stats: bool = False):
+    """Causal varlen prefill attention with per-group precision routing.
+
+    Steps for each (sequence, query head h, query-tile row r), in the pages'
+    order:
+      * kv = h // (Hq/Hkv): query heads of one KV head share its routing word
+        ([Explainer, 支持的场景]; reading: contiguous head groups);
+      * for each legal key tile t, group G = t // g, bit = (word >> G) & 1
+        ([Digest, method]; [Map, hot loop]);
+      * bit 1: S = int32(Q_i8 K_i8^T) * fl32(fl32(s_q s_k) / sqrt(d)); bit 0:
+        S = (Q K^T) * fl32(1/sqrt(d)) -- both in one floating score domain
+        ([Digest, method]; [Explainer, 第三步]);
+      * causal and sequence-end masking regardless of the bit ([Digest,
+        method]);
+      * one softmax over the row's scores -- the shared online-softmax state
+        of the fused kernel reaches the same value ([Routes, precision
+        routing]; [Map, hot loop]);
+      * P.V with both operands in FP16 ([Digest, method]: V and PV stay FP16):
+        reading: P is rounded to binary16 and the normaliser sums the same
+        rounded P (``round_p=False`` keeps P unrounded).
+
+    ``rows``: optional iterable of (seq, head, r) to evaluate (others stay 0).
+    Returns float64 O [T, Hq, d] (and, with ``return_stats``, a dict of
+    per-row P sums keyed by (seq, head, r)).
+    """
+    cu = [int(c) for c in cu_seqlens]
+    seqlens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    T, _, d = q.shape
+    if hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    grp = hq // hkv
+    qt_off, kt_off = _tile_offsets(seqlens)
+    inv_sqrt_d = softmax_scale(d)
+    out = np.zeros((T, hq, d), dtype=np.float64)
+    stats = {}
+    if rows is None:
+        rows = [(s, h, r) for s in range(len(seqlens)) for h in range(hq)
+                for r in range(seq_geometry(seqlens[s]).Tm)]
+    geos = {}
+    for (s, h, r) in rows:
+        L = seqlens[s]
+        geo = geos.get(L) or geos.setdefault(L, seq_geometry(L))
+        start = cu[s]
+        kv = h // grp
+        word = int(words[kv, qt_off[s] + r])
+        q0, q1 = BLOCK_M * r, min(BLOCK_M * r + BLOCK_M, L)
+        nq = q1 - q0
+        nk = geo.last_tile[r] * BLOCK_N + BLOCK_N
+        nk = min(nk, L)
+        S = np.empty((nq, nk), dtype=np.float64)
+        qf = q[start + q0:start + q1, h, :].astype(np.float64)
+        qi = q_i8[start + q0:start + q1, h, :].astype(np.float64)
+        sq = q_scale[h, qt_off[s] + r]
+        for t in range(geo.last_tile[r] + 1):
+            G = t // geo.g
+            bit = (word >> G) & 1
+            k0, k1 = BLOCK_N * t, min(BLOCK_N * t + BLOCK_N, L)
+            if bit:
+                # integer products summed exactly (|sum| < 2^24 < 2^53)
+                acc = qi @ k_i8[start + k0:start + k1, kv, :].astype(np.float64).T
+                c = int8_tile_scale(sq, k_scale[kv, kt_off[s] + t], d)
+                S[:, k0:k1] = acc * np.float64(c)
+            else:
+                kf = k[start + k0:start + k1, kv, :].astype(np.float64)
+                S[:, k0:k1] = (qf @ kf.T) * np.float64(inv_sqrt_d)
+        qpos = np.arange(q0, q1)[:, None]
+        kpos = np.arange(nk)[None, :]
+        S = np.where(kpos <= qpos, S, -np.inf)
+        m = S.max(axis=1, keepdims=True)
+        p = np.exp(S - m)
+        if round_p:
+            p = p.astype(np.float16).astype(np.float64)
+        l = p.sum(axis=1, keepdims=True)
+        vf = v[start:start + nk, kv, :].astype(np.float64)
+        out[start + q0:start + q1, h, :] = (p @ vf) / l
+        if return_stats:
+            stats[(s, h, r)] = (p / l).sum(axis=1)
+    if return_stats:
+        return out, stats
+    return out
+
+
+def run(q, k, v, cu_seqlens, hq: int, hkv: int, template: str, coverage_bp: int,
+        seed: int = 0, rows=None, round_p: bool = True):
+    """Whole path: routing words, quantised Q/K and scales, fp64 output."""
+    cu = [int(c) for c in cu_seqlens]
+    seqlens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    words, g, n8, nl = routing_words(seqlens, hkv, template, coverage_bp, seed)
+    q_i8, q_scale = quantize_blocks(q, cu, BLOCK_M)
+    k_i8, k_scale = quantize_blocks(k, cu, BLOCK_N)
+    o = prefill_attention(q, k, v, q_i8, k_i8, q_scale, k_scale, words, cu, hq, hkv,
+                          rows=rows, round_p=round_p)
+    return dict(words=words, g=g, n_int8=n8, n_legal=nl, q_i8=q_i8, k_i8=k_i8,
+                q_scale=q_scale, k_scale=k_scale, out=o)

@@ -1,0 +1,94 @@
+"""Seeded synthetic workloads for TileMix prefill attention.
+
+This module only draws inputs (shapes, value distributions, packing); it holds
+none of the attention, routing or quantisation arithmetic.  Both the HIP path
+and the CPU oracle consume exactly the bytes produced here.
+
+Workloads stand in for the attention layers the TileMix pages measure
+(LLaMA 3.2 3B: Hq=24, Hkv=8, d=128; Qwen-2-7B: Hq=28, Hkv=4, d=128) with
+synthetic N(0,1) activations; the pages' own tasks (LongEval, LV-Eval) are not
+used.  Recipe:
+
+* ``rng = numpy.random.default_rng(seed)`` (PCG64);
+* Q, K, V drawn as float32 standard normal, in that order, with shapes
+  [T, Hq, d], [T, Hkv, d], [T, Hkv, d] (T = total packed tokens);
+* when ``outliers`` is set, ``chan = rng.choice(d, 4, replace=False)`` and the
+  same four channels of Q and K are multiplied by 10 (in float32);
+* everything is then rounded to float16 (round-to-nearest-even).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Template ids shared by every layer of the stack (C-ABI, binding, oracle).
+TEMPLATE_IDS = {
+    "band": 0,
+    "global": 1,
+    "rowrandom": 2,
+    "alignedsparse": 3,
+    "bigbird": 4,
+    "sptrans": 5,
+}
+TEMPLATE_NAMES = {v: k for k, v in TEMPLATE_IDS.items()}
+
+# Named workloads.  ``template``/``coverage_bp`` are the routing settings the
+# workload is quoted with; sweeps override them.
+WORKLOADS = {
+    "tiny": dict(seqlens=[256], hq=1, hkv=1, d=64, outliers=False,
+                 template="band", coverage_bp=5000),
+    "llama3b_l1k": dict(seqlens=[1024] * 8, hq=24, hkv=8, d=128, outliers=True,
+                        template="sptrans", coverage_bp=2500),
+    "llama3b_l4k": dict(seqlens=[4096] * 8, hq=24, hkv=8, d=128, outliers=True,
+                        template="sptrans", coverage_bp=7500),
+    "llama3b_l8k": dict(seqlens=[8192] * 8, hq=24, hkv=8, d=128, outliers=True,
+                        template="sptrans", coverage_bp=7500),
+    "qwen2_7b_varlen": dict(seqlens=[65536, 16384, 8192, 4096, 1024, 1024], hq=28,
+                            hkv=4, d=128, outliers=True, template="rowrandom",
+                            coverage_bp=5000),
+}
+
+
+def cu_seqlens_of(seqlens) -> np.ndarray:
+    """Prefix sums [0, L0, L0+L1, ...] as int32."""
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(np.asarray(seqlens, dtype=np.int64))
+    if cu[-1] > np.iinfo(np.int32).max:
+        raise ValueError("total token count does not fit int32")
+    return cu.astype(np.int32)
+
+
+def make_qkv(seqlens, hq: int, hkv: int, d: int, outliers: bool, seed: int = 0):
+    """Draw packed fp16 Q, K, V ([T, H, d], token-major) and cu_seqlens."""
+    cu = cu_seqlens_of(seqlens)
+    t = int(cu[-1])
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((t, hq, d), dtype=np.float32)
+    k = rng.standard_normal((t, hkv, d), dtype=np.float32)
+    v = rng.standard_normal((t, hkv, d), dtype=np.float32)
+    if outliers:
+        chan = rng.choice(d, 4, replace=False)
+        q[..., chan] *= np.float32(10.0)
+        k[..., chan] *= np.float32(10.0)
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16), cu
+
+
+def make_workload(name: str, seed: int = 0):
+    """Inputs of a named workload: (q, k, v, cu_seqlens, spec dict)."""
+    spec = dict(WORKLOADS[name])
+    q, k, v, cu = make_qkv(spec["seqlens"], spec["hq"], spec["hkv"], spec["d"],
+                           spec["outliers"], seed)
+    return q, k, v, cu, spec
+
+
+def lossless_blocks(seqlens, heads: int, d: int, block: int, seed: int = 0):
+    """Values k * 2^-6 with integer k in [-127, 127] and one entry of +-127 per
+    (block, head): blockwise absmax/127 quantisation reproduces them exactly."""
+    cu = cu_seqlens_of(seqlens)
+    rng = np.random.default_rng(seed)
+    ints = rng.integers(-127, 128, size=(int(cu[-1]), heads, d))
+    for s in range(len(seqlens)):
+        start, end = int(cu[s]), int(cu[s + 1])
+        for b0 in range(start, end, block):
+            ints[b0, :, 0] = 127 * np.where(rng.random(heads) < 0.5, -1, 1)
+    return (ints.astype(np.float32) * np.float32(2.0 ** -6)).astype(np.float16)
