@@ -1,0 +1,164 @@
+/*
+ * tilemix.h -- C ABI of the MI355X (gfx950) TileMix prefill library.
+ *
+ * TileMix is causal dense prefill attention in one fused streaming kernel in
+ * which every hardware-aligned score-tile group computes Q.K^T either in FP16
+ * or in blockwise INT8, and all groups share one online-softmax state.
+ *
+ * Sources (web pages about TileMix), cited by title and section:
+ *   [Digest]    "TileMix: Tile-Centric Mixed-Precision Attention for LLM
+ *               Inference Acceleration" (paper digest), method and setup.
+ *   [Explainer] "TileMix：给AI大模型的“注意力”做一次精准的精度分配手术"
+ *               (popular explainer), sections 第一步 / 第二步 / 第三步 / 支持的场景.
+ *   [Routes]    "TileMix Routes Attention Precision at the Hardware-Tile
+ *               Level", section "Precision routing over score tiles".
+ *   [Map]       "Precision Has a Map: TileMix Routes INT8 Inside Dense
+ *               Attention", section "The routing mechanism is designed to stay
+ *               inside the hot loop".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are token-major and contiguous: Q, O are [T, Hq, d], K, V are
+ *    [T, Hkv, d]; sequences are packed back to back (cu_seqlens: B+1 int32
+ *    prefix sums, cu_seqlens[0] = 0, non-decreasing).  FP16 is IEEE binary16.
+ *  - Score tiles are TILEMIX_BLOCK_M query rows x TILEMIX_BLOCK_N keys,
+ *    counted from each sequence's first token.  Per sequence of length L:
+ *    Tm = ceil(L/128) query tiles, Tn = ceil(L/64) key tiles, grouping factor
+ *    g = max(1, ceil(Tn/64)); routing group G of a row holds key tiles
+ *    G*g .. G*g+g-1.  Global tile indices concatenate the sequences' tiles in
+ *    batch order (sequence s starts at sum of Tm / Tn of sequences < s).
+ *  - Head dims supported: 64 and 128.  Query head h reads KV head
+ *    h / (Hq/Hkv) (GQA with contiguous groups).
+ *  - The caller owns every buffer.  Entry points taking device pointers only
+ *    enqueue work on `hip_stream` (a hipStream_t; NULL = the null stream) and
+ *    never synchronise; they allocate no device memory.
+ *  - Every pointer must be non-NULL (unless its count is 0) and 16-byte
+ *    aligned.  All validation happens on the host before any launch.
+ *  - Return value: TILEMIX_OK (0) or a negative TILEMIX_E* code; then
+ *    tilemix_last_error() describes the failure.  No C++ exception crosses
+ *    the ABI.
+ */
+#ifndef TILEMIX_H
+#define TILEMIX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TILEMIX_BLOCK_M 128   /* query rows per score tile and per Q quant block */
+#define TILEMIX_BLOCK_N 64    /* keys per score tile and per K quant block      */
+#define TILEMIX_WORD_BITS 64  /* routing groups per query-tile row, at most     */
+
+enum tilemix_status {
+  TILEMIX_OK = 0,
+  TILEMIX_EINVAL = -1,       /* bad argument (null/misaligned pointer, range)  */
+  TILEMIX_EUNSUPPORTED = -2, /* head_dim not in {64, 128}, plan version, ...   */
+  TILEMIX_EHIP = -3          /* a HIP runtime call or launch failed             */
+};
+
+/* Static routing templates ([Digest, method]: Band keeps the diagonal-local
+ * region in FP16, Global keeps designated positions, Row-Random keeps a random
+ * FP16 subset per row, Aligned-Sparse extends right-aligned, BigBird is the
+ * union of the first three, SpTrans is stride plus tail). */
+enum tilemix_template {
+  TILEMIX_BAND = 0,
+  TILEMIX_GLOBAL = 1,
+  TILEMIX_ROWRANDOM = 2,
+  TILEMIX_ALIGNEDSPARSE = 3,
+  TILEMIX_BIGBIRD = 4,
+  TILEMIX_SPTRANS = 5
+};
+
+/* Message of the last failure on the calling thread ("" if none).  The string
+ * stays valid until the next call of a tilemix function on this thread. */
+const char* tilemix_last_error(void);
+
+/* Sizes of a packed batch (host only).
+ * cu_seqlens_h: host int32[batch+1].  Outputs (host, any may be NULL):
+ * total tokens T, total query tiles sum(Tm), total key tiles sum(Tn). */
+int tilemix_query_sizes(const int32_t* cu_seqlens_h, int32_t batch, int64_t* total_tokens,
+                        int64_t* total_q_tiles, int64_t* total_k_tiles);
+
+/* Routing words (host only) -- [Digest, method]: one bit per routing group
+ * (1 = INT8, 0 = FP16), one 64-bit word per (KV head, query-tile row), looked
+ * up with a shift and a mask ([Map, hot loop]); coverage is the INT8 share of
+ * legal tile groups; a static template is reused across layers, batch entries
+ * and KV heads.
+ *
+ * A group (r, G) is legal when it holds a pair with key <= query inside the
+ * sequence.  The template orders a sequence's legal groups; the first
+ * N_legal - N8 stay FP16 and the last N8 = floor((coverage_bp * N_legal +
+ * 5000) / 10000) go INT8.  Bit G of a word is group G (LSB = group 0); bits of
+ * illegal groups are 0.  `seed` feeds Row-Random (and BigBird) only.
+ *
+ * Outputs (host buffers owned by the caller):
+ *   words_h        uint64[num_kv_heads][total_q_tiles] (same for every head)
+ *   g_h            int32[batch]     grouping factor per sequence (may be NULL)
+ *   int8_groups_h  int64[batch]     N8 per sequence (may be NULL)
+ *   legal_groups_h int64[batch]     N_legal per sequence (may be NULL)
+ * Errors: EINVAL for coverage outside [0, 10000], unknown template, bad
+ * cu_seqlens or null words_h with a non-empty batch. */
+int tilemix_build_routing(const int32_t* cu_seqlens_h, int32_t batch, int32_t num_kv_heads,
+                          int32_t tmpl, int32_t coverage_bp, uint64_t seed, uint64_t* words_h,
+                          int32_t* g_h, int64_t* int8_groups_h, int64_t* legal_groups_h);
+
+/* Work plan (host only) -- the geometry and schedule of one packed batch:
+ * per-sequence tile offsets and grouping factors, plus the ordered list of
+ * (sequence, query head, query-tile row) work units the fused kernel runs,
+ * longest rows first and grouped so that units sharing a KV head run on the
+ * same accelerator complex die.  The plan is an opaque array of int32; the
+ * caller keeps a host copy and uploads an identical device copy (both are
+ * passed to the device entry points).  It depends only on (cu_seqlens, Hq,
+ * Hkv, head_dim) and can be reused across layers and calls.
+ * tilemix_plan_size returns its length in int32 elements in *plan_len. */
+int tilemix_plan_size(const int32_t* cu_seqlens_h, int32_t batch, int32_t hq, int32_t hkv,
+                      int32_t head_dim, int64_t* plan_len);
+int tilemix_build_plan(const int32_t* cu_seqlens_h, int32_t batch, int32_t hq, int32_t hkv,
+                       int32_t head_dim, int32_t* plan_h, int64_t plan_len);
+
+/* Blockwise symmetric quantiser (device) -- [Digest, method]: only Q and K are
+ * quantised, in blocks of 128 x d (Q) and 64 x d (K), symmetric with scale =
+ * absmax / 127.  Per (head, block): a = max|x|, s = a / 127 and q =
+ * round-half-even(x / s) clamped to [-127, 127], both divisions IEEE binary32;
+ * a = 0 gives s = 0 and q = 0.  A block at a sequence end holds only that
+ * sequence's rows.
+ * Inputs:  q_f16 [T, Hq, d], k_f16 [T, Hkv, d] (device).
+ * Outputs: q_i8 [T, Hq, d], k_i8 [T, Hkv, d] (device int8),
+ *          q_scale float[Hq][total_q_tiles], k_scale float[Hkv][total_k_tiles]. */
+int tilemix_quantize_qk(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                        const void* k_f16, int8_t* q_i8, int8_t* k_i8, float* q_scale,
+                        float* k_scale, void* hip_stream);
+
+/* Fused mixed-precision causal prefill (device) -- [Digest, method]; [Routes,
+ * precision routing]; [Map, hot loop].  For every legal key tile t of query
+ * tile row r, bit = (word >> (t / g)) & 1 selects the score path:
+ *   bit 1: S = float(int32 sum of q_i8 * k_i8) * (s_q * s_k / sqrt(d))
+ *   bit 0: S = (fp16 Q . fp16 K, fp32 accumulation) / sqrt(d)
+ * then the causal / sequence-end mask (independent of the bit), one shared
+ * online softmax (running max, normaliser, output accumulator in fp32), and
+ * P.V with P rounded to fp16 and V fp16 (fp32 accumulation).  O = acc / l is
+ * written as fp16 (round-to-nearest-even).
+ * words_d: device uint64[Hkv][total_q_tiles] from tilemix_build_routing (bits
+ * of illegal groups are never read).  q_i8/k_i8/q_scale/k_scale from
+ * tilemix_quantize_qk.  out_f16: device [T, Hq, d]. */
+int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                           const void* k_f16, const void* v_f16, const int8_t* q_i8,
+                           const int8_t* k_i8, const float* q_scale, const float* k_scale,
+                           const uint64_t* words_d, void* out_f16, void* hip_stream);
+
+/* Test hook (device): the int32 accumulator of one 128 x 64 INT8 score tile
+ * (sequence seq, query head, query-tile row r, key tile t), computed by the
+ * same device routine the fused kernel uses ([Digest, method]: INT8 MMA with
+ * INT32 accumulation).  Entries whose query or key lies outside the sequence
+ * are 0.  acc_d: device int32[128][64]. */
+int tilemix_debug_qk_i32_tile(const int32_t* plan_h, const int32_t* plan_d, const int8_t* q_i8,
+                              const int8_t* k_i8, int32_t seq, int32_t head, int32_t r,
+                              int32_t t, int32_t* acc_d, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEMIX_H */

@@ -1,0 +1,223 @@
+"""Python binding of libtilemix, the MI355X (gfx950) TileMix prefill library.
+
+Argument marshalling only: every step of the path (routing words, work plan,
+quantisation, fused attention) runs inside libtilemix.so -- the host steps in
+its C++ half, the device steps in its HIP kernels.  PyTorch supplies device
+memory and the current HIP stream.  The functions carry the names of the C
+entry points declared in include/tilemix.h; ``TileMixPrefill`` bundles them
+for one packed batch shape.
+
+The library must be built first (``python -m mixed_precision_attention_amd.build``);
+importing works without it, but every call raises ``TileMixError`` when the
+shared library is missing -- there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtilemix.so")
+
+BLOCK_M = 128
+BLOCK_N = 64
+
+TEMPLATE_IDS = {"band": 0, "global": 1, "rowrandom": 2, "alignedsparse": 3, "bigbird": 4,
+                "sptrans": 5}
+
+_STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EHIP"}
+
+
+class TileMixError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"tilemix {_STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+
+_SIGNATURES = {
+    "tilemix_last_error": ([], ctypes.c_char_p),
+    "tilemix_query_sizes": ([_P, _I32, _P, _P, _P], ctypes.c_int),
+    "tilemix_build_routing": ([_P, _I32, _I32, _I32, _I32, _U64, _P, _P, _P, _P], ctypes.c_int),
+    "tilemix_plan_size": ([_P, _I32, _I32, _I32, _I32, _P], ctypes.c_int),
+    "tilemix_build_plan": ([_P, _I32, _I32, _I32, _I32, _P, _I64], ctypes.c_int),
+    "tilemix_quantize_qk": ([_P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "tilemix_prefill_varlen": ([_P] * 12, ctypes.c_int),
+    "tilemix_debug_qk_i32_tile": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtilemix.so (raises TileMixError when it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise TileMixError(-3, f"{LIB_PATH} is not built; run "
+                                   "`python -m mixed_precision_attention_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        msg = lib().tilemix_last_error()
+        raise TileMixError(rc, msg.decode() if msg else "")
+
+
+def _host_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _hptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data) if a.size else None
+
+
+def _dptr(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous torch tensor on a GPU."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TileMixError(-1, f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TileMixError(-1, f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise TileMixError(-1, f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ----------------------------------------------------------------- host calls
+
+def tilemix_last_error() -> str:
+    msg = lib().tilemix_last_error()
+    return msg.decode() if msg else ""
+
+
+def tilemix_query_sizes(cu_seqlens):
+    cu = _host_i32(cu_seqlens)
+    out = (ctypes.c_int64 * 3)()
+    _check(lib().tilemix_query_sizes(_hptr(cu), len(cu) - 1, ctypes.byref(out, 0),
+                                     ctypes.byref(out, 8), ctypes.byref(out, 16)))
+    return int(out[0]), int(out[1]), int(out[2])
+
+
+def tilemix_build_routing(cu_seqlens, num_kv_heads: int, template, coverage_bp: int, seed: int = 0):
+    """Returns (words uint64 [Hkv, sum Tm], g int32 [B], n_int8 int64 [B], n_legal int64 [B])."""
+    cu = _host_i32(cu_seqlens)
+    batch = len(cu) - 1
+    tmpl = TEMPLATE_IDS[template] if isinstance(template, str) else int(template)
+    _, tq, _ = tilemix_query_sizes(cu)
+    words = np.zeros((max(num_kv_heads, 0), tq), dtype=np.uint64)
+    g = np.zeros(batch, dtype=np.int32)
+    n8 = np.zeros(batch, dtype=np.int64)
+    nl = np.zeros(batch, dtype=np.int64)
+    _check(lib().tilemix_build_routing(_hptr(cu), batch, int(num_kv_heads), tmpl, int(coverage_bp),
+                                       ctypes.c_uint64(seed & (2 ** 64 - 1)), _hptr(words),
+                                       _hptr(g), _hptr(n8), _hptr(nl)))
+    return words, g, n8, nl
+
+
+def tilemix_build_plan(cu_seqlens, hq: int, hkv: int, head_dim: int) -> np.ndarray:
+    cu = _host_i32(cu_seqlens)
+    n = ctypes.c_int64(0)
+    _check(lib().tilemix_plan_size(_hptr(cu), len(cu) - 1, hq, hkv, head_dim, ctypes.byref(n)))
+    plan = np.zeros(n.value, dtype=np.int32)
+    _check(lib().tilemix_build_plan(_hptr(cu), len(cu) - 1, hq, hkv, head_dim, _hptr(plan), n.value))
+    return plan
+
+
+# --------------------------------------------------------------- device calls
+
+def tilemix_quantize_qk(plan_h, plan_d, q, k, q_i8, k_i8, q_scale, k_scale, stream=None):
+    import torch
+    _check(lib().tilemix_quantize_qk(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
+        _dptr(k, torch.float16, "k"), _dptr(q_i8, torch.int8, "q_i8"), _dptr(k_i8, torch.int8, "k_i8"),
+        _dptr(q_scale, torch.float32, "q_scale"), _dptr(k_scale, torch.float32, "k_scale"),
+        _stream(stream)))
+
+
+def tilemix_prefill_varlen(plan_h, plan_d, q, k, v, q_i8, k_i8, q_scale, k_scale, words_d, out,
+                           stream=None):
+    import torch
+    _check(lib().tilemix_prefill_varlen(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
+        _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(q_i8, torch.int8, "q_i8"),
+        _dptr(k_i8, torch.int8, "k_i8"), _dptr(q_scale, torch.float32, "q_scale"),
+        _dptr(k_scale, torch.float32, "k_scale"), _dptr(words_d, torch.int64, "words_d"),
+        _dptr(out, torch.float16, "out"), _stream(stream)))
+
+
+def tilemix_debug_qk_i32_tile(plan_h, plan_d, q_i8, k_i8, seq: int, head: int, r: int, t: int,
+                              acc, stream=None):
+    import torch
+    _check(lib().tilemix_debug_qk_i32_tile(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q_i8, torch.int8, "q_i8"),
+        _dptr(k_i8, torch.int8, "k_i8"), seq, head, r, t, _dptr(acc, torch.int32, "acc"),
+        _stream(stream)))
+
+
+# ------------------------------------------------------------------ bundle
+
+class TileMixPrefill:
+    """One packed batch shape: host/device plan, routing words and the
+    quantised-operand buffers, reused across calls (the pages reuse a static
+    template across layers, batch entries and KV heads)."""
+
+    def __init__(self, cu_seqlens, hq: int, hkv: int, head_dim: int, template, coverage_bp: int,
+                 seed: int = 0, device="cuda"):
+        import torch
+        self.cu = _host_i32(cu_seqlens)
+        self.hq, self.hkv, self.d = hq, hkv, head_dim
+        self.tokens, self.tq, self.tk = tilemix_query_sizes(self.cu)
+        self.plan_h = tilemix_build_plan(self.cu, hq, hkv, head_dim)
+        self.plan_d = torch.from_numpy(self.plan_h).to(device)
+        self.device = device
+        self.set_routing(template, coverage_bp, seed)
+        t = max(self.tokens, 1)
+        self.q_i8 = torch.empty((t, hq, head_dim), dtype=torch.int8, device=device)
+        self.k_i8 = torch.empty((t, hkv, head_dim), dtype=torch.int8, device=device)
+        self.q_scale = torch.empty((hq, max(self.tq, 1)), dtype=torch.float32, device=device)
+        self.k_scale = torch.empty((hkv, max(self.tk, 1)), dtype=torch.float32, device=device)
+
+    def set_routing(self, template, coverage_bp: int, seed: int = 0):
+        import torch
+        self.words, self.g, self.n_int8, self.n_legal = tilemix_build_routing(
+            self.cu, self.hkv, template, coverage_bp, seed)
+        w = self.words if self.words.size else np.zeros((1, 1), dtype=np.uint64)
+        self.words_d = torch.from_numpy(w.view(np.int64)).to(self.device)
+
+    def quantize(self, q, k, stream=None):
+        tilemix_quantize_qk(self.plan_h, self.plan_d, q, k, self.q_i8, self.k_i8, self.q_scale,
+                            self.k_scale, stream)
+
+    def attend(self, q, k, v, out, stream=None):
+        tilemix_prefill_varlen(self.plan_h, self.plan_d, q, k, v, self.q_i8, self.k_i8,
+                               self.q_scale, self.k_scale, self.words_d, out, stream)
+
+    def __call__(self, q, k, v, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        self.quantize(q, k, stream)
+        self.attend(q, k, v, out, stream)
+        return out

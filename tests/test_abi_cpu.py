@@ -1,0 +1,143 @@
+"""Host-side checks of libtilemix through its C ABI (no GPU needed): exported
+symbols, routing words bit-exact with the oracle, the work plan, and argument
+validation."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import mixed_precision_attention_amd as tm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tilemix.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tm.LIB_PATH),
+                                reason="libtilemix.so not built (run __graft_entry__.build())")
+
+
+def test_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    names = sorted(set(re.findall(r"\b(tilemix_[a-z0-9_]+)\s*\(", text)))
+    assert len(names) >= 8
+    lib = ctypes.CDLL(tm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("template", oracle.TEMPLATES)
+def test_routing_bit_exact_with_oracle(template):
+    for lens in ([256], [1], [130], [1000], [4096], [8192], [300, 0, 77, 129, 2049],
+                 [16384, 1024]):
+        for cov in (0, 1000, 2500, 5000, 7500, 10000):
+            for seed in (0, 12345):
+                w, g, n8, nl = tm.tilemix_build_routing(synth.cu_seqlens_of(lens), 3, template, cov, seed)
+                ow, og, on8, onl = oracle.routing_words(lens, 3, template, cov, seed)
+                assert np.array_equal(w, ow), (lens, cov, seed)
+                assert np.array_equal(g, og) and np.array_equal(n8, on8) and np.array_equal(nl, onl)
+
+
+def test_routing_large_varlen_matches_oracle():
+    lens = synth.WORKLOADS["qwen2_7b_varlen"]["seqlens"]
+    w, g, n8, nl = tm.tilemix_build_routing(synth.cu_seqlens_of(lens), 4, "rowrandom", 5000, 0)
+    ow, og, on8, onl = oracle.routing_words(lens, 4, "rowrandom", 5000, 0)
+    assert np.array_equal(w, ow) and list(n8) == [8320, 2080, 1040, 528, 36, 36]
+
+
+def test_query_sizes():
+    t, tq, tk = tm.tilemix_query_sizes([0, 256, 256, 386])
+    assert (t, tq, tk) == (386, 2 + 0 + 2, 4 + 0 + 3)
+
+
+def _plan_parts(plan):
+    hdr = plan[:16]
+    batch, hq, hkv = hdr[2], hdr[3], hdr[4]
+    seqtab = plan[hdr[10]:hdr[10] + 8 * batch].reshape(batch, 8)
+    items = plan[hdr[11]:hdr[11] + 2 * hdr[9]].reshape(-1, 2)
+    return hdr, seqtab, items
+
+
+@pytest.mark.parametrize("lens,hq,hkv", [([4096] * 8, 24, 8), ([65536, 16384, 8192, 4096, 1024, 1024], 28, 4),
+                                         ([300, 0, 77, 129, 1], 6, 2), ([256], 1, 1)])
+def test_plan_covers_every_unit_once(lens, hq, hkv):
+    cu = synth.cu_seqlens_of(lens)
+    plan = tm.tilemix_build_plan(cu, hq, hkv, 128)
+    hdr, seqtab, items = _plan_parts(plan)
+    assert hdr[0] == 0x544D5850 and hdr[6] == cu[-1]
+    qt = kt = 0
+    for s, L in enumerate(lens):
+        geo = oracle.seq_geometry(L)
+        assert list(seqtab[s][:7]) == [cu[s], L, qt, kt, geo.g, geo.Tm, geo.Tn]
+        qt += geo.Tm
+        kt += geo.Tn
+    assert (hdr[7], hdr[8]) == (qt, kt)
+    real = [(int(a), int(b) >> 16, int(b) & 0xffff) for a, b in items if a >= 0]
+    expect = {(s, h, r) for s, L in enumerate(lens) for h in range(hq)
+              for r in range(oracle.seq_geometry(L).Tm)}
+    assert len(real) == len(expect) and set(real) == expect
+    # units sharing a (sequence, KV head) are dealt to few dies; each die's
+    # queue runs its longest rows first
+    die = {}
+    for pos, (a, b) in enumerate(items):
+        if a < 0:
+            continue
+        r = int(b) & 0xffff
+        geo = oracle.seq_geometry(lens[a])
+        die.setdefault(pos % 8, []).append(geo.last_tile[r] + 1)
+    for costs in die.values():
+        assert costs == sorted(costs, reverse=True)
+
+
+def test_errors_are_reported():
+    cu = synth.cu_seqlens_of([256])
+    with pytest.raises(tm.TileMixError, match="coverage_bp"):
+        tm.tilemix_build_routing(cu, 1, "band", 10001)
+    with pytest.raises(tm.TileMixError, match="template"):
+        tm.tilemix_build_routing(cu, 1, 9, 100)
+    with pytest.raises(tm.TileMixError, match="non-decreasing"):
+        tm.tilemix_build_routing([0, 10, 5], 1, "band", 100)
+    with pytest.raises(tm.TileMixError, match="cu_seqlens\\[0\\]"):
+        tm.tilemix_query_sizes([3, 10])
+    with pytest.raises(tm.TileMixError, match="Hq"):
+        tm.tilemix_build_plan(cu, 5, 2, 128)
+    with pytest.raises(tm.TileMixError, match="head_dim") as e:
+        tm.tilemix_build_plan(cu, 2, 2, 96)
+    assert e.value.code == -2
+    lib = tm.lib()
+    plan = tm.tilemix_build_plan(cu, 2, 1, 64)
+    p = ctypes.c_void_p(plan.ctypes.data)
+    fake = ctypes.c_void_p(16)
+    odd = ctypes.c_void_p(24)
+    # pointer validation happens before any device work
+    assert lib.tilemix_quantize_qk(p, None, fake, fake, fake, fake, fake, fake, None) == -1
+    assert "plan_d" in tm.tilemix_last_error()
+    assert lib.tilemix_prefill_varlen(p, fake, fake, fake, fake, fake, odd, fake, fake, fake, fake, None) == -1
+    assert "aligned" in tm.tilemix_last_error()
+    bad = plan.copy()
+    bad[0] = 7
+    assert lib.tilemix_prefill_varlen(ctypes.c_void_p(bad.ctypes.data), fake, fake, fake, fake, fake, fake,
+                                      fake, fake, fake, fake, None) == -1
+    assert "not a TileMix plan" in tm.tilemix_last_error()
+    assert lib.tilemix_debug_qk_i32_tile(p, fake, fake, fake, 0, 0, 5, 0, fake, None) == -1
+    assert "row" in tm.tilemix_last_error()
+    bad = plan.copy()
+    bad[1] = 99
+    assert lib.tilemix_quantize_qk(ctypes.c_void_p(bad.ctypes.data), fake, fake, fake, fake, fake, fake, fake,
+                                   None) == -2
+
+
+def test_empty_batch_is_a_no_op():
+    cu = np.array([0, 0], dtype=np.int32)
+    w, g, n8, nl = tm.tilemix_build_routing(cu, 2, "band", 5000)
+    assert w.shape == (2, 0) and list(nl) == [0]
+    plan = tm.tilemix_build_plan(cu, 2, 2, 64)
+    lib = tm.lib()
+    p = ctypes.c_void_p(plan.ctypes.data)
+    fake = ctypes.c_void_p(16)
+    # nothing to launch: returns OK without touching device pointers
+    assert lib.tilemix_prefill_varlen(p, fake, None, None, None, None, None, None, None, None, None, None) == 0
+    assert lib.tilemix_quantize_qk(p, fake, None, None, None, None, None, None, None) == 0
