@@ -1,0 +1,230 @@
+"""Benchmark of the TileMix fused prefill path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--template T] [--coverage BP] [--no-cpu-baseline]
+
+One step = one pass of the device hot path over one packed batch: the
+blockwise Q/K quantiser followed by the fused mixed-precision prefill kernel.
+Routing words and the work plan are static per batch shape (the pages reuse
+one template across layers, batch entries and KV heads) and are built once,
+outside the timed region; their host build time is reported separately.
+
+Prints ONE JSON line.  ``value`` is whole-job attention tokens/s with inputs
+resident in HBM.  ``roofline`` refers to the fused prefill kernel: achieved
+fp16-equivalent TFLOP/s (INT8 operations weighted by the fp16/int8 peak
+ratio) against the published MI355X dense fp16 MFMA peak, i.e. ``frac`` is
+the coverage-weighted MFMA roofline time over the measured kernel time.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16 = 2.5e15   # MI355X dense fp16 MFMA, FLOP/s (published)
+PEAK_I8 = 5.0e15    # MI355X dense int8 MFMA, OP/s (published)
+METRIC = "prefill attn tokens/s + % of MFMA roofline, 3B shape L=4k B=8 SpTrans75"
+KERNEL_SRC = os.path.join(ROOT, "mixed_precision_attention_amd", "csrc", "tilemix_kernels.hip")
+
+
+def legal_pair_counts(cu, words, hq, hkv):
+    """(P, P8): legal causal (query, key) pairs over all query heads, and the
+    ones lying in INT8-routed groups -- counted exactly from the words."""
+    import numpy as np
+    P = P8 = 0
+    row_off = 0
+    for s in range(len(cu) - 1):
+        L = int(cu[s + 1] - cu[s])
+        Tm, Tn = -(-L // 128), -(-L // 64)
+        g = max(1, -(-Tn // 64))
+        for r in range(Tm):
+            q = np.arange(128 * r, min(128 * r + 128, L))
+            last_t = int(q[-1]) // 64
+            t = np.arange(last_t + 1)
+            # keys of tile t visible to query q: clip(q - 64 t + 1, 0, 64)
+            cnt = np.clip(q[:, None] - 64 * t[None, :] + 1, 0, 64).sum(axis=0)
+            w = np.uint64(words[0, row_off + r])
+            bits = ((w >> (t // g).astype(np.uint64)) & np.uint64(1)).astype(np.int64)
+            P += int(cnt.sum())
+            P8 += int((cnt * bits).sum())
+        row_off += Tm
+    return P * hq, P8 * hq
+
+
+def traffic_record(path):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or the kernel source changed since."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec
+
+
+def cpu_baseline(q, k, v, cu, spec, template, coverage, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the workload: the
+    full quantiser pass plus sampled work units of the attention,
+    extrapolated to the whole batch by legal-pair count."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    words, g, n8, nl = oracle.routing_words(np.diff(cu).tolist(), spec["hkv"], template, coverage, 0)
+    q_i8, q_s = oracle.quantize_blocks(q, cu, oracle.BLOCK_M)
+    k_i8, k_s = oracle.quantize_blocks(k, cu, oracle.BLOCK_N)
+    t_prep = time.perf_counter() - t0
+    lens = np.diff(cu)
+    rng = np.random.default_rng(0)
+    units = [(s, h, r) for s in range(len(lens)) for h in range(spec["hq"])
+             for r in range(-(-int(lens[s]) // 128))]
+    order = rng.permutation(len(units))
+    done, pairs, t_attn = [], 0, 0.0
+    for i in order:
+        s, h, r = units[i]
+        t1 = time.perf_counter()
+        oracle.prefill_attention(q, k, v, q_i8, k_i8, q_s, k_s, words, cu, spec["hq"], spec["hkv"],
+                                 rows=[(s, h, r)])
+        t_attn += time.perf_counter() - t1
+        L = int(lens[s])
+        qpos = np.arange(128 * r, min(128 * r + 128, L))
+        pairs += int((qpos + 1).sum())
+        done.append((s, h, r))
+        if t_attn + t_prep > budget_s:
+            break
+    total_pairs = sum(int(L) * (int(L) + 1) // 2 for L in lens) * spec["hq"]
+    t_total = t_prep + t_attn * total_pairs / pairs
+    tokens = int(cu[-1])
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"routing + full quantiser pass ({t_prep:.1f}s) + {len(done)} of {len(units)} "
+                       f"(sequence, head, query-tile) units of attention ({t_attn:.1f}s, "
+                       f"{pairs / total_pairs:.2%} of legal pairs), extrapolated by legal-pair count")}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3b_l4k")
+    ap.add_argument("--template", default=None)
+    ap.add_argument("--coverage", type=int, default=None, help="INT8 coverage in basis points")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the TileMix path has no "
+              "cross-GPU work; the sharding design is described in DESIGN.md.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mixed_precision_attention_amd as tm
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    q, k, v, cu, spec = synth.make_workload(args.workload)
+    template = args.template or spec["template"]
+    coverage = spec["coverage_bp"] if args.coverage is None else args.coverage
+    hq, hkv, d = spec["hq"], spec["hkv"], spec["d"]
+
+    t0 = time.perf_counter()
+    tp = tm.TileMixPrefill(cu, hq, hkv, d, template, coverage)
+    host_build_ms = (time.perf_counter() - t0) * 1e3
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        tp.quantize(qd, kd)
+        tp.attend(qd, kd, vd, out)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        tp.quantize(qd, kd)
+        ev[i][1].record(stream)
+        tp.attend(qd, kd, vd, out)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    quant_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    ms_per_step = total_ms / K
+    tokens = int(cu[-1])
+    value = tokens / (ms_per_step * 1e-3)
+
+    P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
+    t_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
+    frac = t_roof / (attn_ms * 1e-3)
+    flops_eq = t_roof * PEAK_F16
+    achieved = flops_eq / (attn_ms * 1e-3) / 1e12
+    traffic = None
+    rec = traffic_record(os.path.join(ROOT, "profiles", f"prefill_{args.workload}_traffic.json"))
+    if rec is not None:
+        traffic = rec["hbm_bytes_per_launch"]
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16+i8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}_{template}{coverage // 100}",
+                   "seqlens": spec["seqlens"] if len(set(spec["seqlens"])) > 1 else
+                   f"{len(spec['seqlens'])}x{spec['seqlens'][0]}",
+                   "hq": hq, "hkv": hkv, "head_dim": d, "template": template,
+                   "coverage_bp": coverage, "tokens": tokens},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_F16 / 1e12,
+                     "unit": "TFLOP/s", "frac": frac, "traffic": traffic},
+        "breakdown": {"quantize_ms": quant_ms, "prefill_ms": attn_ms,
+                      "legal_pairs": P, "int8_pairs": P8, "int8_pair_share": P8 / P,
+                      "int8_tops": 2 * d * P8 / (attn_ms * 1e-3) / 1e12,
+                      "fp16_tflops": 2 * d * (2 * P - P8) / (attn_ms * 1e-3) / 1e12,
+                      "roofline_us": t_roof * 1e6, "host_build_ms": host_build_ms,
+                      "wall_s": wall},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(q, k, v, cu, spec, template, coverage, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

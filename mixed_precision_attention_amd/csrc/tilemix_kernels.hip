@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "tilemix.h"
 #include "tilemix_host.h"
@@ -147,54 +148,95 @@ __global__ __launch_bounds__(kThreads) void quantize_qk_kernel(QuantArgs a) {
 
 // --------------------------------------------------------------------------
 // Fused prefill pieces shared by the kernel and the int32 tile hook.
+//
+// LDS holds two tile buffers (double buffering); a buffer is one K tile
+// (fp16, or int8 on INT8-routed tiles) followed by one fp16 V tile, 64 rows
+// each.  Tiles arrive by direct buffer->LDS loads (buffer_load_dwordx4 ...
+// lds): lane i of a wave writes bytes [16 i, 16 i + 16) of a 1 KiB window.
+// A tile of R rows per window uses NW = 64 / R windows; row r lives in
+// window r % NW at slot r / NW, and consecutive windows are kWinPad bytes
+// further apart than 1 KiB.  Rows r .. r+NW-1 therefore start on shifted
+// banks, which makes the fragment reads below conflict-free with purely
+// additive addresses (lane part + compile-time offset):
+//   K rows (fp16 or int8): window pitch 1040 B -> 16 consecutive rows at one
+//     16-byte column start 4 banks apart;
+//   V rows: window pitch 1088 B -> the 4 rows x 64 B read by 32 lanes of a
+//     transposed read start 16 banks apart.
 // --------------------------------------------------------------------------
-template <int D>
-struct Lds {
-  static constexpr int kKStride = D + 8;     // halfs per fp16 K row (pads 16 B)
-  static constexpr int kK8Stride = D + 16;   // bytes per int8 K row (pads 16 B)
-  static constexpr int kVStride = D + 16;    // halfs per V row (pads 32 B)
-  static constexpr int kKBytes = kBlockN * kKStride * 2;
-  static constexpr int kVBytes = kBlockN * kVStride * 2;
+template <int kRowBytes, int kPitch>
+struct Layout {
+  static constexpr int kRowsPerWin = 1024 / kRowBytes;
+  static constexpr int kWins = kBlockN / kRowsPerWin;
+  static constexpr int kBytes = kWins * kPitch;
+  static constexpr int kLanesPerRow = kRowBytes / 16;
+  // LDS byte offset of (row, byte column) within the tile.
+  __device__ static constexpr int at(int row, int col) {
+    return (row % kWins) * kPitch + (row / kWins) * kRowBytes + col;
+  }
+  // Lane part of the source offset of this lane's 16 bytes in every window
+  // (window j adds j * row stride).
+  __device__ static int lane_src(int lane, int gstride) {
+    return (lane / kLanesPerRow) * kWins * gstride + (lane % kLanesPerRow) * 16;
+  }
+  // Issue the tile whose first row is at `base`; rows >= nvalid repeat row
+  // nvalid - 1 of the same sequence (finite; those keys are masked).
+  __device__ static void issue(char* lds_tile, const void* base, int gstride, int nvalid, int wave,
+                               int lane, int lane_off) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+    int off = lane_off;
+    if (nvalid < kBlockN) {
+      // last tile of a sequence: clamp the row, window by window below
+      off = (lane % kLanesPerRow) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < (kWins + 3) / 4; ++i) {
+      const int j = wave + 4 * i;
+      if (j < kWins) {
+        int o = off, so = j * gstride;
+        if (nvalid < kBlockN) {
+          const int r = min(j + (lane / kLanesPerRow) * kWins, nvalid - 1);
+          o = r * gstride + (lane % kLanesPerRow) * 16;
+          so = 0;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, lds_tile + j * kPitch), 16, o, so, 0, 0);
+      }
+    }
+  }
 };
 
-// Stage one 64-key tile of int8 K into LDS; rows past the sequence end are 0.
 template <int D>
-__device__ inline void stage_k_i8(char* sK, const int8_t* k_rows, int row_stride, int nvalid) {
-  constexpr int kChunksPerRow = D / 16;
-  constexpr int kChunks = kBlockN * kChunksPerRow;
-  for (int idx = threadIdx.x; idx < kChunks; idx += kThreads) {
-    const int r = idx / kChunksPerRow, cc = idx % kChunksPerRow;
-    int4v v = {0, 0, 0, 0};
-    if (r < nvalid) v = *reinterpret_cast<const int4v*>(k_rows + (size_t)r * row_stride + cc * 16);
-    *reinterpret_cast<int4v*>(sK + r * Lds<D>::kK8Stride + cc * 16) = v;
-  }
-}
+struct Tile {
+  using K16 = Layout<2 * D, 1040>;
+  using K8 = Layout<D, 1040>;
+  using V = Layout<2 * D, 1088>;
+  static constexpr int kKRegion = K16::kBytes > K8::kBytes ? K16::kBytes : K8::kBytes;
+  static constexpr int kBuf = kKRegion + V::kBytes;
+  static constexpr int kLds = 2 * kBuf;
+};
 
-// Stage one 64-row fp16 tile (K or V) into LDS with the given row stride.
-template <int D, int kStride>
-__device__ inline void stage_f16(_Float16* sX, const _Float16* rows, int row_stride, int nvalid) {
-  constexpr int kChunksPerRow = D / 8;
-  constexpr int kChunks = kBlockN * kChunksPerRow;
-  for (int idx = threadIdx.x; idx < kChunks; idx += kThreads) {
-    const int r = idx / kChunksPerRow, cc = idx % kChunksPerRow;
-    half8 v = {};
-    if (r < nvalid) v = *reinterpret_cast<const half8*>(rows + (size_t)r * row_stride + cc * 8);
-    *reinterpret_cast<half8*>(sX + r * kStride + cc * 8) = v;
-  }
+__device__ inline void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wave-uniform read-only scalar: read through the constant address space so
+// it becomes a scalar load (waited on by lgkmcnt, not vmcnt, so it does not
+// wait for the tile loads in flight).
+__device__ inline float load_uniform(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)(p);
 }
 
 // INT8 path of one wave's 64 x 32 score block: S^T = K_i8 . Q_i8^T with int32
 // accumulation ([Digest, method]: INT8 MMA, INT32 accumulation).
 template <int D>
 __device__ inline void qk_tile_i8(const char* sK, const int4v* qb, int16v acc[2]) {
+  using K8 = typename Tile<D>::K8;
   const int lane = threadIdx.x & 63, c = lane & 31, hh = lane >> 5;
+  const char* base = sK + K8::at(c, hh * 16);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     int16v a = {};
-    const char* row = sK + (kb * 32 + c) * Lds<D>::kK8Stride + hh * 16;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      const int4v kf = *reinterpret_cast<const int4v*>(row + kk * 32);
+      const int4v kf = *reinterpret_cast<const int4v*>(base + K8::at(kb * 32, kk * 32));
       a = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qb[kk], a, 0, 0, 0);
     }
     acc[kb] = a;
@@ -203,15 +245,16 @@ __device__ inline void qk_tile_i8(const char* sK, const int4v* qb, int16v acc[2]
 
 // FP16 path of the same block: S^T = K . Q^T, fp32 accumulation.
 template <int D>
-__device__ inline void qk_tile_f16(const _Float16* sK, const half8* qf, float16v acc[2]) {
+__device__ inline void qk_tile_f16(const char* sK, const half8* qf, float16v acc[2]) {
+  using K16 = typename Tile<D>::K16;
   const int lane = threadIdx.x & 63, c = lane & 31, hh = lane >> 5;
+  const char* base = sK + K16::at(c, hh * 16);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     float16v a = {};
-    const _Float16* row = sK + (kb * 32 + c) * Lds<D>::kKStride + hh * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const half8 kf = *reinterpret_cast<const half8*>(row + kk * 16);
+      const half8 kf = *reinterpret_cast<const half8*>(base + K16::at(kb * 32, kk * 32));
       a = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], a, 0, 0, 0);
     }
     acc[kb] = a;
@@ -243,7 +286,15 @@ __device__ inline void load_q(const _Float16* qrow, const int8_t* q8row, bool va
 // Per legal key tile: routing bit lookup ([Map, hot loop]: shift and mask),
 // QK^T on the routed path, rescale into the common score domain ([Explainer,
 // 第三步]), causal/sequence-end mask, shared online softmax, P.V in FP16
-// ([Digest, method]).
+// ([Digest, method]).  Tile t+1 streams into the other LDS buffer while tile
+// t is computed; one barrier per tile.  Tiles before the row's diagonal need
+// no mask and run in a separate loop.
+//
+// Online softmax in the log2 domain: x = S * log2(e).  The running maximum m
+// is raised only when a row's tile maximum exceeds it by more than kLazy
+// (then O and l are rescaled); otherwise P = 2^(x - m) <= 2^kLazy, which
+// fp16 holds exactly as well as any P <= 1.  O / l does not depend on the m
+// chosen, so this changes rounding only.
 // --------------------------------------------------------------------------
 struct PrefillArgs {
   const int32_t* plan;
@@ -259,10 +310,115 @@ struct PrefillArgs {
   int32_t hq, hkv, tq, tk;
 };
 
+constexpr float kLazy = 8.0f;
+
+template <int D>
+struct RowState {
+  float m, lsum;
+  float16v o[D / 32];
+};
+
+template <int D, bool kMasked>
+__device__ __forceinline__ void tile_step(const char* buf, int bit, float f_i8, float f16s, const half8* qf,
+                                          const int4v* qb, RowState<D>& st, int k0, int qi, int L) {
+  const int lane = threadIdx.x & 63, hh = lane >> 5;
+  float16v accv[2];
+  float f;
+  if (bit) {
+    int16v acc[2];
+    qk_tile_i8<D>(buf, qb, acc);
+    f = f_i8;
+    // exact: |acc| <= 127^2 d < 2^24
+    accv[0] = __builtin_convertvector(acc[0], float16v);
+    accv[1] = __builtin_convertvector(acc[1], float16v);
+  } else {
+    qk_tile_f16<D>(buf, qf, accv);
+    f = f16s;
+  }
+  float accf[2][16];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) accf[kb][i] = accv[kb][i];
+  // Causal / sequence-end mask, independent of the routing bit: masked
+  // entries become -inf here and P = 0 below (even when f = 0).
+  if (kMasked) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+        if (key > qi || key >= L) accf[kb][i] = -INFINITY;
+      }
+  }
+  // Row maximum of the raw accumulators (f >= 0 preserves the order).
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, accf[kb][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = (mx == -INFINITY) ? -INFINITY : mx * f;
+  const bool raise = mx > st.m + kLazy;
+  if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rescale the lanes that need it
+    const float m_new = raise ? mx : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
+  }
+  const float negm = -st.m;
+  uint32_t pw[2][8];
+  float psum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(accf[kb][2 * i], f, negm));
+      float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(accf[kb][2 * i + 1], f, negm));
+      if (kMasked) {
+        e0 = accf[kb][2 * i] == -INFINITY ? 0.f : e0;
+        e1 = accf[kb][2 * i + 1] == -INFINITY ? 0.f : e1;
+      }
+      const half2v pk = {(_Float16)e0, (_Float16)e1};
+      psum = __builtin_amdgcn_fdot2(pk, (half2v){(_Float16)1.0f, (_Float16)1.0f}, psum, false);
+      pw[kb][i] = __builtin_bit_cast(uint32_t, pk);
+    }
+  st.lsum += psum;
+
+  // O^T += V^T . P^T (fp16 operands, fp32 accumulation).  V fragments come
+  // transposed from LDS: a 16-lane group gives lane i the column i of 4
+  // consecutive rows.
+  using VL = typename Tile<D>::V;
+  const int j = lane & 15, sub = (lane >> 4) & 1;
+  // rows ks*16 + x (+8), x = hh*4 + j/4 < 8: window and slot split into a
+  // lane part and a compile-time part because 16 and 8 are multiples of the
+  // window count's divisors used here (NW = 16 or 8).
+  const char* vbase = buf + Tile<D>::kKRegion + VL::at(hh * 4 + (j >> 2), (sub * 16 + 4 * (j & 3)) * 2);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int kb = ks >> 1, hf = ks & 1;
+    const half8 pf = __builtin_bit_cast(half8, (uint4){pw[kb][hf * 4 + 0], pw[kb][hf * 4 + 1],
+                                                       pw[kb][hf * 4 + 2], pw[kb][hf * 4 + 3]});
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const char* a0 = vbase + VL::at(ks * 16, db * 64);
+      const char* a1 = vbase + VL::at(ks * 16 + 8, db * 64);
+      // Whole-vector casts: element-wise extraction of the transposed
+      // read's result is mis-assembled by this compiler.
+      const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(short4v, a0)));
+      const half4 hi = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(short4v, a1)));
+      const half8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, st.o[db], 0, 0, 0);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char sK[Lds<D>::kKBytes];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[kBlockN * Lds<D>::kVStride];
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  using T = Tile<D>;
 
   const int32_t* item = a.plan + a.plan[kItemOff] + kItemStride * blockIdx.x;
   const int seq = item[0];
@@ -276,111 +432,66 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int last_tile = min(q0 + kBlockM - 1, L - 1) / kBlockN;
   const uint64_t word = a.words[(size_t)kv * a.tq + qt_off + row];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, c = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = q0 + 32 * w + c;  // this lane's query (sequence-local)
   const bool qvalid = qi < L;
+
+  const int s16 = a.hkv * D * 2, s8 = a.hkv * D;  // bytes between consecutive K/V rows
+  const char* kseq = reinterpret_cast<const char*>(a.k + ((size_t)start * a.hkv + kv) * D);
+  const char* k8seq = reinterpret_cast<const char*>(a.ki8 + ((size_t)start * a.hkv + kv) * D);
+  const char* vseq = reinterpret_cast<const char*>(a.v + ((size_t)start * a.hkv + kv) * D);
+  const int lo16 = T::K16::lane_src(lane, s16), lo8 = T::K8::lane_src(lane, s8);
+  const int lov = T::V::lane_src(lane, s16);
+
+  // Routing bit of tile t: (word >> (t / g)) & 1, tracked incrementally.
+  int grp = 0, in_grp = 0;  // group of the current tile, position in it
+  auto issue = [&](int t, int bit, char* buf) {
+    const int nvalid = min(kBlockN, L - t * kBlockN);
+    if (bit) T::K8::issue(buf, k8seq + (size_t)t * kBlockN * s8, s8, nvalid, w, lane, lo8);
+    else T::K16::issue(buf, kseq + (size_t)t * kBlockN * s16, s16, nvalid, w, lane, lo16);
+    T::V::issue(buf + T::kKRegion, vseq + (size_t)t * kBlockN * s16, s16, nvalid, w, lane, lov);
+  };
+  issue(0, (int)(word & 1ull), smem);
 
   half8 qf[D / 16];
   int4v qb[D / 32];
   load_q<D>(a.q + ((size_t)(start + qi) * a.hq + head) * D,
             a.qi8 + ((size_t)(start + qi) * a.hq + head) * D, qvalid, qf, qb);
-  const float sq = a.qs[(size_t)head * a.tq + qt_off + row];
+  const float sq = load_uniform(a.qs + (size_t)head * a.tq + qt_off + row);
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
   const float scale16 = inv_sqrt_d * kLog2e;
+  const float* kscale = a.ks + (size_t)kv * a.tk + kt_off;
 
-  float m = -INFINITY, lsum = 0.f;
-  float16v o[D / 32];
+  RowState<D> st;
+  st.m = -INFINITY;
+  st.lsum = 0.f;
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = (float16v){};
+  for (int i = 0; i < D / 32; ++i) st.o[i] = (float16v){};
 
-  const int kv_stride = a.hkv * D;
-  for (int t = 0; t <= last_tile; ++t) {
-    const int bit = (int)((word >> (t / g)) & 1ull);
-    const int k0 = t * kBlockN;
-    const int nvalid = min(kBlockN, L - k0);
-    const size_t krow = ((size_t)(start + k0) * a.hkv + kv) * D;
-    __syncthreads();  // previous tile's LDS reads are done
-    if (bit) stage_k_i8<D>(sK, a.ki8 + krow, kv_stride, nvalid);
-    else stage_f16<D, Lds<D>::kKStride>(reinterpret_cast<_Float16*>(sK), a.k + krow, kv_stride, nvalid);
-    stage_f16<D, Lds<D>::kVStride>(sV, a.v + krow, kv_stride, nvalid);
-    __syncthreads();
-
-    // Scores of this wave's 32 queries x 64 keys, in the log2 domain.
-    float x[2][16];
-    if (bit) {
-      int16v acc[2];
-      qk_tile_i8<D>(sK, qb, acc);
-      const float sk = a.ks[(size_t)kv * a.tk + kt_off + t];
-      const float f = (sq * sk) * inv_sqrt_d * kLog2e;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[kb][i] = (float)acc[kb][i] * f;
-    } else {
-      float16v acc[2];
-      qk_tile_f16<D>(reinterpret_cast<const _Float16*>(sK), qf, acc);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[kb][i] = acc[kb][i] * scale16;
-    }
-    // Causal / sequence-end mask, independent of the routing bit.
-    if (k0 + kBlockN - 1 > q0 || k0 + kBlockN > L) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          if (key > qi || key >= L) x[kb][i] = -INFINITY;
-        }
-    }
-    // Shared online softmax state.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    half8 p[2][2];
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const half2v pk = {(_Float16)__builtin_amdgcn_exp2f(x[kb][i] - m_new),
-                           (_Float16)__builtin_amdgcn_exp2f(x[kb][i + 1] - m_new)};
-        psum = __builtin_amdgcn_fdot2(pk, (half2v){(_Float16)1.0f, (_Float16)1.0f}, psum, false);
-        p[kb][i >> 3][i & 7] = pk[0];
-        p[kb][i >> 3][(i & 7) + 1] = pk[1];
-      }
-    lsum = lsum * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-
-    // O^T += V^T . P^T (fp16 operands, fp32 accumulation).
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kbase = ks * 16;
-      const int j = lane & 15, sub = (lane >> 4) & 1;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const _Float16* p0 = sV + (kbase + hh * 4 + (j >> 2)) * Lds<D>::kVStride + db * 32 + sub * 16 + 4 * (j & 3);
-        // Whole-vector casts: element-wise extraction of the transposed
-        // read's result is mis-assembled by this compiler.
-        const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(short4v, p0)));
-        const half4 hi = __builtin_bit_cast(
-            half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(short4v, p0 + 8 * Lds<D>::kVStride)));
-        const half8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, p[ks >> 1][ks & 1], o[db], 0, 0, 0);
-      }
-    }
-  }
+  // One pipelined step: wait for tile t, start tile t+1, compute tile t.
+  auto step = [&](int t, auto masked) {
+    char* buf = smem + (t & 1) * T::kBuf;
+    const int bit = (int)((word >> grp) & 1ull);
+    const int ngrp = (in_grp + 1 == g) ? grp + 1 : grp;
+    in_grp = (in_grp + 1 == g) ? 0 : in_grp + 1;
+    wait_tile_loads();
+    __syncthreads();  // tile t visible; everyone is done with tile t-1's buffer
+    if (t < last_tile) issue(t + 1, (int)((word >> ngrp) & 1ull), smem + ((t + 1) & 1) * T::kBuf);
+    grp = ngrp;
+    const float f_i8 = (sq * load_uniform(kscale + t)) * inv_sqrt_d * kLog2e;
+    tile_step<D, decltype(masked)::value>(buf, bit, f_i8, scale16, qf, qb, st, t * kBlockN, qi, L);
+  };
+  // Tiles t < 2 row lie entirely below the diagonal of every query of the
+  // work unit and inside the sequence: no mask.  The rest (the diagonal
+  // tiles and a partial last tile) run in a second loop.
+  int t = 0;
+  for (; t < 2 * row; ++t) step(t, std::false_type{});
+  for (; t <= last_tile; ++t) step(t, std::true_type{});
 
   // Epilogue: O = acc / l, fp16 round-to-nearest-even.
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const int hh = lane >> 5;
+  const float ltot = st.lsum + __shfl_xor(st.lsum, 32);
   const float inv = 1.0f / ltot;
   if (qvalid) {
     _Float16* orow = a.out + ((size_t)(start + qi) * a.hq + head) * D;
@@ -390,27 +501,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int i4 = 0; i4 < 4; ++i4) {
         half4 h;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = (_Float16)(o[db][i4 * 4 + e] * inv);
+        for (int e = 0; e < 4; ++e) h[e] = (_Float16)(st.o[db][i4 * 4 + e] * inv);
         *reinterpret_cast<half4*>(orow + db * 32 + i4 * 8 + hh * 4) = h;
       }
   }
 }
 
-// Int32 accumulator of one INT8 score tile, through the kernel's own
-// staging and qk_tile_i8 routine.
+// Int32 accumulator of one INT8 score tile, through the kernel's own tile
+// loader and qk_tile_i8 routine.
 template <int D>
 __global__ __launch_bounds__(kThreads) void debug_qk_i32_kernel(const int32_t* plan, const int8_t* qi8,
                                                                 const int8_t* ki8, int seq, int head,
                                                                 int row, int t, int32_t* acc_out) {
-  __shared__ __attribute__((aligned(16))) char sK[Lds<D>::kKBytes];
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char sK[T::K8::kBytes];
   const int hq = plan[kHq], hkv = plan[kHkv];
   const int32_t* rec = plan + kHeaderLen + seq * kSeqStride;
   const int start = rec[kSeqStart], L = rec[kSeqLen];
   const int kv = head / (hq / hkv);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, c = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = row * kBlockM + 32 * w + c;
   const int k0 = t * kBlockN;
-  stage_k_i8<D>(sK, ki8 + ((size_t)(start + k0) * hkv + kv) * D, hkv * D, max(0, min(kBlockN, L - k0)));
+  const int nvalid = min(kBlockN, L - k0);
+  const int s8 = hkv * D;
+  T::K8::issue(sK, ki8 + ((size_t)(start + k0) * hkv + kv) * D, s8, nvalid, w, lane,
+               T::K8::lane_src(lane, s8));
   int4v qb[D / 32];
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
@@ -419,6 +535,7 @@ __global__ __launch_bounds__(kThreads) void debug_qk_i32_kernel(const int32_t* p
       v = *reinterpret_cast<const int4v*>(qi8 + ((size_t)(start + qi) * hq + head) * D + kk * 32 + hh * 16);
     qb[kk] = v;
   }
+  wait_tile_loads();
   __syncthreads();
   int16v acc[2];
   qk_tile_i8<D>(sK, qb, acc);
@@ -427,7 +544,8 @@ __global__ __launch_bounds__(kThreads) void debug_qk_i32_kernel(const int32_t* p
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-      acc_out[(32 * w + c) * kBlockN + key] = acc[kb][i];
+      // keys past the sequence end hold a repeated row in LDS: report 0
+      acc_out[(32 * w + c) * kBlockN + key] = (k0 + key < L) ? acc[kb][i] : 0;
     }
 }
 
@@ -523,9 +641,9 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const unsigned grid = (unsigned)plan_h[kNumItems];
   if (plan_h[kHeadDim] == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3(grid), dim3(kThreads), Tile<64>::kLds, st, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3(grid), dim3(kThreads), Tile<128>::kLds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return TILEMIX_OK;
