@@ -163,6 +163,26 @@ __global__ __launch_bounds__(kThreads) void quantize_qk_kernel(QuantArgs a) {
 //   V rows: window pitch 1088 B -> the 4 rows x 64 B read by 32 lanes of a
 //     transposed read start 16 banks apart.
 // --------------------------------------------------------------------------
+// Buffer resource for raw (unstrided) byte addressing from `base`.
+__device__ inline int4v make_rsrc(const void* base) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  return (int4v){(int)__builtin_amdgcn_readfirstlane((unsigned)b),
+                 (int)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32) & 0xffffu), 0x7fffffff, 0x00020000};
+}
+
+// One direct buffer->LDS load: every lane's 16 bytes at (voffset + soffset)
+// land at lds_dst + 16 * lane.  Written as inline asm on purpose: the
+// compiler's own form makes every later LDS read wait for all such loads in
+// flight (it cannot tell the two tile buffers apart), which would serialise
+// the prefetch.  Completion is awaited explicitly (wait_tile_loads) before the
+// barrier that publishes the tile.
+__device__ inline void lds_dma16(char* lds_dst, int4v rsrc, int voffset, int soffset) {
+  const unsigned la = __builtin_amdgcn_readfirstlane((unsigned)(size_t)LDS_PTR(char, lds_dst));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(la), "v"(voffset),
+               "s"(rsrc), "s"(soffset)
+               : "memory", "m0");
+}
+
 template <int kRowBytes, int kPitch>
 struct Layout {
   static constexpr int kRowsPerWin = 1024 / kRowBytes;
@@ -182,24 +202,22 @@ struct Layout {
   // nvalid - 1 of the same sequence (finite; those keys are masked).
   __device__ static void issue(char* lds_tile, const void* base, int gstride, int nvalid, int wave,
                                int lane, int lane_off) {
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
-    int off = lane_off;
-    if (nvalid < kBlockN) {
-      // last tile of a sequence: clamp the row, window by window below
-      off = (lane % kLanesPerRow) * 16;
-    }
+    const int4v rsrc = make_rsrc(base);
+    if (nvalid == kBlockN) {
 #pragma unroll
-    for (int i = 0; i < (kWins + 3) / 4; ++i) {
-      const int j = wave + 4 * i;
-      if (j < kWins) {
-        int o = off, so = j * gstride;
-        if (nvalid < kBlockN) {
+      for (int i = 0; i < (kWins + 3) / 4; ++i) {
+        const int j = wave + 4 * i;
+        if (j < kWins) lds_dma16(lds_tile + j * kPitch, rsrc, lane_off, j * gstride);
+      }
+    } else {
+      // last tile of a sequence: clamp the row
+#pragma unroll
+      for (int i = 0; i < (kWins + 3) / 4; ++i) {
+        const int j = wave + 4 * i;
+        if (j < kWins) {
           const int r = min(j + (lane / kLanesPerRow) * kWins, nvalid - 1);
-          o = r * gstride + (lane % kLanesPerRow) * 16;
-          so = 0;
+          lds_dma16(lds_tile + j * kPitch, rsrc, r * gstride + (lane % kLanesPerRow) * 16, 0);
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, lds_tile + j * kPitch), 16, o, so, 0, 0);
       }
     }
   }
@@ -212,8 +230,19 @@ struct Tile {
   using V = Layout<2 * D, 1088>;
   static constexpr int kKRegion = K16::kBytes > K8::kBytes ? K16::kBytes : K8::kBytes;
   static constexpr int kBuf = kKRegion + V::kBytes;
-  static constexpr int kLds = 2 * kBuf;
+  static constexpr int kScales = 1024;  // key-tile scales staged per chunk
+  static constexpr int kLds = 2 * kBuf + kScales * 4;
 };
+
+// Combine a value with the same register of lane l ^ 32 (no LDS round trip).
+__device__ inline float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -224,41 +253,79 @@ __device__ inline float load_uniform(const float* p) {
   return *(const __attribute__((address_space(4))) float*)(p);
 }
 
+// The fragment reads below are issued one batch ahead of the matrix
+// instructions that consume them, with scheduling fences so the compiler
+// keeps that order (left alone it sinks each read next to its consumer and
+// exposes the full LDS latency on every instruction).
+#define TM_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 // INT8 path of one wave's 64 x 32 score block: S^T = K_i8 . Q_i8^T with int32
 // accumulation ([Digest, method]: INT8 MMA, INT32 accumulation).
 template <int D>
 __device__ inline void qk_tile_i8(const char* sK, const int4v* qb, int16v acc[2]) {
   using K8 = typename Tile<D>::K8;
+  constexpr int kSteps = D / 32;               // per 32-key block
+  constexpr int kBatch = kSteps < 4 ? kSteps : 4;
+  constexpr int kBatches = 2 * kSteps / kBatch;
   const int lane = threadIdx.x & 63, c = lane & 31, hh = lane >> 5;
   const char* base = sK + K8::at(c, hh * 16);
+  int4v kf[2][kBatch];
+  auto load = [&](int bt, int4v* dst) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    int16v a = {};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const int4v kf = *reinterpret_cast<const int4v*>(base + K8::at(kb * 32, kk * 32));
-      a = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qb[kk], a, 0, 0, 0);
+    for (int i = 0; i < kBatch; ++i) {
+      const int step = bt * kBatch + i, kb = step / kSteps, kk = step % kSteps;
+      dst[i] = *reinterpret_cast<const int4v*>(base + K8::at(kb * 32, kk * 32));
     }
-    acc[kb] = a;
+  };
+  acc[0] = (int16v){};
+  acc[1] = (int16v){};
+  load(0, kf[0]);
+#pragma unroll
+  for (int bt = 0; bt < kBatches; ++bt) {
+    TM_FENCE();
+    if (bt + 1 < kBatches) load(bt + 1, kf[(bt + 1) & 1]);
+    TM_FENCE();
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int step = bt * kBatch + i, kb = step / kSteps, kk = step % kSteps;
+      acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[bt & 1][i], qb[kk], acc[kb], 0, 0, 0);
+    }
   }
+  TM_FENCE();
 }
 
 // FP16 path of the same block: S^T = K . Q^T, fp32 accumulation.
 template <int D>
 __device__ inline void qk_tile_f16(const char* sK, const half8* qf, float16v acc[2]) {
   using K16 = typename Tile<D>::K16;
+  constexpr int kSteps = D / 16;               // per 32-key block
+  constexpr int kBatch = 4;
+  constexpr int kBatches = 2 * kSteps / kBatch;
   const int lane = threadIdx.x & 63, c = lane & 31, hh = lane >> 5;
   const char* base = sK + K16::at(c, hh * 16);
+  half8 kf[2][kBatch];
+  auto load = [&](int bt, half8* dst) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    float16v a = {};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const half8 kf = *reinterpret_cast<const half8*>(base + K16::at(kb * 32, kk * 32));
-      a = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], a, 0, 0, 0);
+    for (int i = 0; i < kBatch; ++i) {
+      const int step = bt * kBatch + i, kb = step / kSteps, kk = step % kSteps;
+      dst[i] = *reinterpret_cast<const half8*>(base + K16::at(kb * 32, kk * 32));
     }
-    acc[kb] = a;
+  };
+  acc[0] = (float16v){};
+  acc[1] = (float16v){};
+  load(0, kf[0]);
+#pragma unroll
+  for (int bt = 0; bt < kBatches; ++bt) {
+    TM_FENCE();
+    if (bt + 1 < kBatches) load(bt + 1, kf[(bt + 1) & 1]);
+    TM_FENCE();
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int step = bt * kBatch + i, kb = step / kSteps, kk = step % kSteps;
+      acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[bt & 1][i], qf[kk], acc[kb], 0, 0, 0);
+    }
   }
+  TM_FENCE();
 }
 
 // Query fragments of this lane's query row (zeros outside the sequence).
@@ -357,7 +424,7 @@ __device__ __forceinline__ void tile_step(const char* buf, int bit, float f_i8, 
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, accf[kb][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_with_other_half(mx);
   mx = (mx == -INFINITY) ? -INFINITY : mx * f;
   const bool raise = mx > st.m + kLazy;
   if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rescale the lanes that need it
@@ -393,14 +460,10 @@ __device__ __forceinline__ void tile_step(const char* buf, int bit, float f_i8, 
   using VL = typename Tile<D>::V;
   const int j = lane & 15, sub = (lane >> 4) & 1;
   // rows ks*16 + x (+8), x = hh*4 + j/4 < 8: window and slot split into a
-  // lane part and a compile-time part because 16 and 8 are multiples of the
-  // window count's divisors used here (NW = 16 or 8).
+  // lane part and a compile-time part (the window count is 16 or 8).
   const char* vbase = buf + Tile<D>::kKRegion + VL::at(hh * 4 + (j >> 2), (sub * 16 + 4 * (j & 3)) * 2);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int kb = ks >> 1, hf = ks & 1;
-    const half8 pf = __builtin_bit_cast(half8, (uint4){pw[kb][hf * 4 + 0], pw[kb][hf * 4 + 1],
-                                                       pw[kb][hf * 4 + 2], pw[kb][hf * 4 + 3]});
+  half8 vf[2][D / 32];
+  auto load_v = [&](int ks, half8* dst) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const char* a0 = vbase + VL::at(ks * 16, db * 64);
@@ -409,10 +472,23 @@ __device__ __forceinline__ void tile_step(const char* buf, int bit, float f_i8, 
       // read's result is mis-assembled by this compiler.
       const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(short4v, a0)));
       const half4 hi = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(short4v, a1)));
-      const half8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, st.o[db], 0, 0, 0);
+      dst[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+  };
+  load_v(0, vf[0]);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    TM_FENCE();
+    if (ks + 1 < 4) load_v(ks + 1, vf[(ks + 1) & 1]);
+    TM_FENCE();
+    const int kb = ks >> 1, hf = ks & 1;
+    const half8 pf = __builtin_bit_cast(half8, (uint4){pw[kb][hf * 4 + 0], pw[kb][hf * 4 + 1],
+                                                       pw[kb][hf * 4 + 2], pw[kb][hf * 4 + 3]});
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[ks & 1][db], pf, st.o[db], 0, 0, 0);
   }
+  TM_FENCE();
 }
 
 template <int D>
@@ -458,10 +534,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   int4v qb[D / 32];
   load_q<D>(a.q + ((size_t)(start + qi) * a.hq + head) * D,
             a.qi8 + ((size_t)(start + qi) * a.hq + head) * D, qvalid, qf, qb);
+  // Let the compiler see the query loads complete here: it does not count the
+  // asm-issued tile loads, so a wait it placed later for these would also
+  // wait for every tile load in flight.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   const float sq = load_uniform(a.qs + (size_t)head * a.tq + qt_off + row);
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
   const float scale16 = inv_sqrt_d * kLog2e;
+  // The row's key-tile scales go through LDS (1024 tiles per chunk): a scalar
+  // load per tile would make every later lgkmcnt wait include its memory
+  // latency.
   const float* kscale = a.ks + (size_t)kv * a.tk + kt_off;
+  float* sks = reinterpret_cast<float*>(smem + 2 * T::kBuf);
+  auto stage_scales = [&](int t0) {
+    const int n = min(T::kScales, last_tile + 1 - t0);
+    for (int i = tid; i < n; i += kThreads) sks[i] = kscale[t0 + i];
+  };
+  stage_scales(0);
 
   RowState<D> st;
   st.m = -INFINITY;
@@ -477,9 +566,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     in_grp = (in_grp + 1 == g) ? 0 : in_grp + 1;
     wait_tile_loads();
     __syncthreads();  // tile t visible; everyone is done with tile t-1's buffer
+    if (t > 0 && (t & (T::kScales - 1)) == 0) {  // next chunk of scales
+      stage_scales(t);
+      __syncthreads();
+    }
     if (t < last_tile) issue(t + 1, (int)((word >> ngrp) & 1ull), smem + ((t + 1) & 1) * T::kBuf);
     grp = ngrp;
-    const float f_i8 = (sq * load_uniform(kscale + t)) * inv_sqrt_d * kLog2e;
+    const float f_i8 = (sq * sks[t & (T::kScales - 1)]) * inv_sqrt_d * kLog2e;
     tile_step<D, decltype(masked)::value>(buf, bit, f_i8, scale16, qf, qb, st, t * kBlockN, qi, L);
   };
   // Tiles t < 2 row lie entirely below the diagonal of every query of the
@@ -491,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   // Epilogue: O = acc / l, fp16 round-to-nearest-even.
   const int hh = lane >> 5;
-  const float ltot = st.lsum + __shfl_xor(st.lsum, 32);
+  const float ltot = sum_with_other_half(st.lsum);
   const float inv = 1.0f / ltot;
   if (qvalid) {
     _Float16* orow = a.out + ((size_t)(start + qi) * a.hq + head) * D;
