@@ -71,6 +71,48 @@ def traffic_record(path):
     return rec
 
 
+def _counter_mean_kib(path, kernel_substr):
+    """Mean per-dispatch value (KiB) of the one counter in a rocprofv3
+    counter_collection.csv, over dispatches whose name contains the text."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if kernel_substr in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of {kernel_substr!r} in {path}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def write_traffic(args):
+    """HBM bytes per prefill launch: FETCH_SIZE and WRITE_SIZE scaled by what
+    the same counters read for a plain copy of known size."""
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.write_traffic
+    kname = "tilemix::prefill_kernel"
+    fetch, nf = _counter_mean_kib(fetch_csv, kname)
+    write, nw = _counter_mean_kib(write_csv, kname)
+    cfetch, _ = _counter_mean_kib(cfetch_csv, "copyBuffer")
+    cwrite, _ = _counter_mean_kib(cwrite_csv, "copyBuffer")
+    f_scale = args.copy_size / (cfetch * 1024)
+    w_scale = args.copy_size / (cwrite * 1024)
+    rec = {
+        "kernel": kname,
+        "workload": args.workload,
+        "kernel_source_sha256": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest(),
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write, "dispatches": [nf, nw],
+        "copy_bytes": args.copy_size, "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "hbm_bytes_per_launch": fetch * 1024 * f_scale + write * 1024 * w_scale,
+        "command": args.profile_command,
+    }
+    out = os.path.join(ROOT, "profiles", f"prefill_{args.workload}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+    return 0
+
+
 def cpu_baseline(q, k, v, cu, spec, template, coverage, budget_s=20.0):
     """The oracle, as it stands, on a bounded sample of the workload: the
     full quantiser pass plus sampled work units of the attention,
@@ -124,7 +166,22 @@ def main(argv=None):
     ap.add_argument("--coverage", type=int, default=None, help="INT8 coverage in basis points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes 5 times "
+                         "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                          "COPY_WRITE_CSV"),
+                    help="no GPU: turn four rocprofv3 --pmc counter_collection.csv files (the prefill "
+                         "run's FETCH_SIZE and WRITE_SIZE, then the --copy-bytes run's) into "
+                         "profiles/prefill_<workload>_traffic.json and exit")
+    ap.add_argument("--copy-size", type=int, default=512 << 20,
+                    help="bytes the --copy-bytes run copied (for --write-traffic)")
+    ap.add_argument("--profile-command", default="",
+                    help="command line recorded in the --write-traffic summary")
     args = ap.parse_args(argv)
+
+    if args.write_traffic:
+        return write_traffic(args)
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the TileMix path has no "
@@ -140,6 +197,16 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 16 * 16
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+        return 0
 
     q, k, v, cu, spec = synth.make_workload(args.workload)
     template = args.template or spec["template"]
