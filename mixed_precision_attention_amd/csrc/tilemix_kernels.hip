@@ -359,7 +359,7 @@ __device__ inline void load_q(const _Float16* qrow, const int8_t* q8row, bool va
 //
 // Online softmax in the log2 domain: x = S * log2(e).  The running maximum m
 // is raised only when a row's tile maximum exceeds it by more than kLazy
-// (then O and l are rescaled); otherwise P = 2^(x - m) <= 2^kLazy, which
+// (then O and l are rescaled); otherwise P = 2^(x - m) <= 2^kLazy = 16384, which
 // fp16 holds exactly as well as any P <= 1.  O / l does not depend on the m
 // chosen, so this changes rounding only.
 // --------------------------------------------------------------------------
@@ -377,7 +377,7 @@ struct PrefillArgs {
   int32_t hq, hkv, tq, tk;
 };
 
-constexpr float kLazy = 8.0f;
+constexpr float kLazy = 14.0f;
 
 template <int D>
 struct RowState {
@@ -427,11 +427,10 @@ __device__ __forceinline__ void tile_step(const char* buf, int bit, float f_i8, 
   mx = max_with_other_half(mx);
   mx = (mx == -INFINITY) ? -INFINITY : mx * f;
   const bool raise = mx > st.m + kLazy;
-  if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rescale the lanes that need it
-    const float m_new = raise ? mx : st.m;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    st.m = m_new;
-    st.lsum *= alpha;
+  const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - mx) : 1.0f;
+  st.m = raise ? mx : st.m;
+  st.lsum *= alpha;
+  if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rescale O where a lane raised
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
   }
