@@ -294,16 +294,13 @@ std::vector<Unit> schedule(const std::vector<SeqGeo>& geos, int32_t hq, int32_t 
     load[d] += part_cost[i];
     die[d].insert(die[d].end(), parts[i].begin(), parts[i].end());
   }
+  // Each die's queue keeps its parts contiguous (largest part first; a part's
+  // units longest first): the units in flight on a die then share one or two
+  // (sequence, KV head) K/V streams, which stay in that die's L2, and the
+  // short units at the end of each part fill the die while the next part's
+  // long ones start.
   size_t longest = 0;
-  for (auto& q : die) {
-    std::stable_sort(q.begin(), q.end(), [](const Unit& a, const Unit& b) {
-      if (a.cost != b.cost) return a.cost > b.cost;
-      if (a.seq != b.seq) return a.seq < b.seq;
-      if (a.head != b.head) return a.head < b.head;
-      return a.row < b.row;
-    });
-    longest = std::max(longest, q.size());
-  }
+  for (auto& q : die) longest = std::max(longest, q.size());
   std::vector<Unit> out;
   out.reserve(longest * kNumXcd);
   for (size_t i = 0; i < longest; ++i)

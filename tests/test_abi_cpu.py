@@ -79,17 +79,29 @@ def test_plan_covers_every_unit_once(lens, hq, hkv):
     expect = {(s, h, r) for s, L in enumerate(lens) for h in range(hq)
               for r in range(oracle.seq_geometry(L).Tm)}
     assert len(real) == len(expect) and set(real) == expect
-    # units sharing a (sequence, KV head) are dealt to few dies; each die's
-    # queue runs its longest rows first
+    # units sharing a (sequence, KV head) are dealt to few dies, in runs that
+    # stay contiguous in the die's queue; each run goes longest row first
     die = {}
     for pos, (a, b) in enumerate(items):
         if a < 0:
             continue
-        r = int(b) & 0xffff
+        h, r = int(b) >> 16, int(b) & 0xffff
         geo = oracle.seq_geometry(lens[a])
-        die.setdefault(pos % 8, []).append(geo.last_tile[r] + 1)
-    for costs in die.values():
-        assert costs == sorted(costs, reverse=True)
+        die.setdefault(pos % 8, []).append(((int(a), h // (hq // hkv)), geo.last_tile[r] + 1))
+    groups_per_die = []
+    for q in die.values():
+        runs = [[q[0]]]
+        for x in q[1:]:
+            if x[0] == runs[-1][-1][0] and x[1] <= runs[-1][-1][1]:
+                runs[-1].append(x)
+            else:
+                runs.append([x])
+        # a group appears in few runs (it is split only when larger than
+        # half a die's share)
+        keys = [r[0][0] for r in runs]
+        assert len(keys) <= 2 * len(set(keys))
+        groups_per_die.append(len(set(keys)))
+    assert max(groups_per_die) <= max(1, -(-len(lens) * hkv // 8)) + 2
 
 
 def test_errors_are_reported():
