@@ -96,6 +96,12 @@ __device__ inline void quantize_block(const _Float16* src, int8_t* dst, float* s
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = __fdiv_rn(amax, 127.0f);
   if (tid == 0) *scale_out = s;
+  // q = round-half-even(fl32(x / s)).  x * fl32(1 / s) is within 2.3e-5 of
+  // fl32(x / s) for |x / s| <= 127 (two roundings of 2^-24 relative each plus
+  // half an ulp of the quotient), so it rounds to the same integer unless it
+  // lies within 2^-15 of a half-integer; only those elements take the exact
+  // IEEE division.
+  const float rs = amax > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int idx = tid + i * kThreads;
@@ -104,11 +110,11 @@ __device__ inline void quantize_block(const _Float16* src, int8_t* dst, float* s
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      int qv = 0;
-      if (amax > 0.f) {
-        const float qf = __builtin_rintf(__fdiv_rn((float)vals[i][j], s));
-        qv = (int)fminf(fmaxf(qf, -127.f), 127.f);
-      }
+      const float x = (float)vals[i][j];
+      const float y = x * rs;
+      float qf = __builtin_rintf(y);
+      if (__builtin_fabsf(y - qf) > 0.5f - 0x1p-15f) qf = __builtin_rintf(__fdiv_rn(x, s));
+      const int qv = (int)__builtin_amdgcn_fmed3f(qf, -127.f, 127.f);
       const uint32_t b = (uint32_t)(qv & 0xff);
       if (j < 4) lo |= b << (8 * j); else hi |= b << (8 * (j - 4));
     }
