@@ -424,6 +424,10 @@ __device__ __forceinline__ void tile_step(const char* buf, int bit, float f_i8, 
         if (key > qi || key >= L) accf[kb][i] = -INFINITY;
       }
   }
+  // The vector-ALU softmax runs at raised wave priority: the sooner it
+  // finishes, the sooner this wave's P.V matrix instructions are ready to
+  // fill the matrix pipe beside the other wave's.
+  __builtin_amdgcn_s_setprio(1);
   // Row maximum of the raw accumulators (f >= 0 preserves the order).
   float mx = -INFINITY;
 #pragma unroll
@@ -458,6 +462,7 @@ __device__ __forceinline__ void tile_step(const char* buf, int bit, float f_i8, 
       pw[kb][i] = __builtin_bit_cast(uint32_t, pk);
     }
   st.lsum += psum;
+  __builtin_amdgcn_s_setprio(0);
 
   // O^T += V^T . P^T (fp16 operands, fp32 accumulation).  V fragments come
   // transposed from LDS: a 16-lane group gives lane i the column i of 4
