@@ -1,8 +1,9 @@
-"""CPU oracle for TileMix prefill attention (test infrastructure only: used by
+"""CPU oracle for TileMix prefill and INT8-cache decode attention (test infrastructure only: used by
 tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg)."""
 from .tilemix_oracle import *  # noqa: F401,F403
 from .tilemix_oracle import (BLOCK_M, BLOCK_N, TEMPLATES, SeqGeometry, seq_geometry,  # noqa: F401
                              int8_group_count, template_order, int8_groups, routing_words,
                              quantize_blocks, qk_int32_tile, prefill_attention, run,
                              splitmix64_mix, rowrandom_hash, sptrans_stride, union_orders,
-                             softmax_scale, int8_tile_scale)
+                             softmax_scale, int8_tile_scale, quantize_kv_cache,
+                             quantize_query_rows, decode_attention)

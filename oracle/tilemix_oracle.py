@@ -1,5 +1,6 @@
 """TileMix oracle -- a plain, slow, CPU-only statement of what the fused
-mixed-precision prefill path computes.
+mixed-precision prefill path computes, and of one decode step against an
+INT8 key/value cache.
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or run this module.  It shares
@@ -463,3 +464,91 @@ def run(q, k, v, cu_seqlens, hq: int, hkv: int, template: str, coverage_bp: int,
                           rows=rows, round_p=round_p)
     return dict(words=words, g=g, n_int8=n8, n_legal=nl, q_i8=q_i8, k_i8=k_i8,
                 q_scale=q_scale, k_scale=k_scale, out=o)
+
+
+# ---------------------------------------------------------------------------
+# Decode against an INT8 key/value cache
+# ---------------------------------------------------------------------------
+#
+# [Explainer, 支持的场景] and [Digest, setup]: besides prefill, TileMix offers
+# an INT8 key/value cache for the generation (decode) side; the pages give no
+# further detail.  Readings taken here:
+#   * the cache stores K and V as int8 with the prefill quantiser's key blocks
+#     (64 x d per head, scale = absmax / 127);
+#   * each decode step has one new query per sequence: the token at position
+#     L - 1, whose own key and value are already in the cache, so it attends
+#     to all L cached positions (no mask is needed);
+#   * the routing word is the prefill word of the query-tile row holding
+#     position L - 1, looked up per key tile as in prefill ([Map, hot loop]);
+#   * bit 1: INT8 query (one scale per sequence and head, a block of one row)
+#     times the INT8 key, int32 accumulation, restored with s_q, s_k and
+#     1/sqrt(d) ([Digest, method]); bit 0: the FP16 query times the
+#     dequantised key k_i8 * s_k, times 1/sqrt(d);
+#   * P is rounded to binary16 as in prefill and multiplies the dequantised
+#     value v_i8 * s_v.
+
+
+def quantize_kv_cache(k, v, cu_seqlens):
+    """INT8 key/value cache: both operands in the key blocks of the prefill
+    quantiser.  Returns (k_i8, k_scale, v_i8, v_scale); scales are
+    float32 [Hkv, total key tiles]."""
+    k_i8, k_scale = quantize_blocks(k, cu_seqlens, BLOCK_N)
+    v_i8, v_scale = quantize_blocks(v, cu_seqlens, BLOCK_N)
+    return k_i8, k_scale, v_i8, v_scale
+
+
+def quantize_query_rows(q):
+    """One new query per sequence, q float16 [B, Hq, d]: the quantiser with
+    blocks of a single row.  Returns (int8 [B, Hq, d], float32 [Hq, B])."""
+    B = q.shape[0]
+    return quantize_blocks(q, list(range(B + 1)), 1)
+
+
+def decode_attention(q, k_i8, k_scale, v_i8, v_scale, words, cu_seqlens, hq: int, hkv: int,
+                     round_p: bool = True):
+    """One decode step against the INT8 cache.
+
+    q: float16 [B, Hq, d], the newest query of each sequence; k_i8, v_i8:
+    int8 [T, Hkv, d] cache (token-major, sequences packed by cu_seqlens, the
+    cache lengths); k_scale, v_scale: float32 [Hkv, total key tiles]; words:
+    the routing words of the cache lengths.  Returns float64 [B, Hq, d];
+    sequences of length 0 give zeros.
+    """
+    cu = [int(c) for c in cu_seqlens]
+    seqlens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    B, _, d = q.shape
+    if B != len(seqlens):
+        raise ValueError("one query per sequence")
+    grp = hq // hkv
+    qt_off, kt_off = _tile_offsets(seqlens)
+    inv_sqrt_d = softmax_scale(d)
+    q_i8, q_scale = quantize_query_rows(q)
+    out = np.zeros((B, hq, d), dtype=np.float64)
+    for s, L in enumerate(seqlens):
+        if L == 0:
+            continue
+        geo = seq_geometry(L)
+        start = cu[s]
+        r = (L - 1) // BLOCK_M
+        for h in range(hq):
+            kv = h // grp
+            word = int(words[kv, qt_off[s] + r])
+            qf = q[s, h, :].astype(np.float64)
+            qi = q_i8[s, h, :].astype(np.float64)
+            S = np.empty(L, dtype=np.float64)
+            vhat = np.empty((L, d), dtype=np.float64)
+            for t in range(geo.Tn):
+                k0, k1 = BLOCK_N * t, min(BLOCK_N * t + BLOCK_N, L)
+                kb = k_i8[start + k0:start + k1, kv, :].astype(np.float64)
+                sk = k_scale[kv, kt_off[s] + t]
+                if (word >> (t // geo.g)) & 1:
+                    S[k0:k1] = (kb @ qi) * np.float64(int8_tile_scale(q_scale[h, s], sk, d))
+                else:
+                    S[k0:k1] = ((kb * np.float64(sk)) @ qf) * np.float64(inv_sqrt_d)
+                vhat[k0:k1] = v_i8[start + k0:start + k1, kv, :].astype(np.float64) * \
+                    np.float64(v_scale[kv, kt_off[s] + t])
+            p = np.exp(S - S.max())
+            if round_p:
+                p = p.astype(np.float16).astype(np.float64)
+            out[s, h, :] = (p @ vhat) / p.sum()
+    return out

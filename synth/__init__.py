@@ -92,3 +92,32 @@ def lossless_blocks(seqlens, heads: int, d: int, block: int, seed: int = 0):
         for b0 in range(start, end, block):
             ints[b0, :, 0] = 127 * np.where(rng.random(heads) < 0.5, -1, 1)
     return (ints.astype(np.float32) * np.float32(2.0 ** -6)).astype(np.float16)
+
+
+def lossless_blocks_pow2(seqlens, heads: int, d: int, block: int, seed: int = 0):
+    """Like ``lossless_blocks`` but every (block, head) has its own
+    power-of-two step 2^-e, e in [3, 9]: values k * 2^-e with one entry of
+    +-127 * 2^-e, so each block's scale differs and is still reproduced
+    exactly."""
+    cu = cu_seqlens_of(seqlens)
+    rng = np.random.default_rng(seed)
+    ints = rng.integers(-127, 128, size=(int(cu[-1]), heads, d)).astype(np.float32)
+    for s in range(len(seqlens)):
+        start, end = int(cu[s]), int(cu[s + 1])
+        for b0 in range(start, end, block):
+            b1 = min(b0 + block, end)
+            ints[b0, :, 0] = 127 * np.where(rng.random(heads) < 0.5, -1, 1)
+            e = rng.integers(3, 10, size=heads).astype(np.float32)
+            ints[b0:b1] *= np.exp2(-e)[None, :, None]
+    return ints.astype(np.float16)
+
+
+def decode_queries(q, cu_seqlens):
+    """The decode query of each sequence: the row of ``q`` at position L - 1
+    (the newest token), [B, H, d]; zeros for an empty sequence."""
+    cu = [int(c) for c in cu_seqlens]
+    out = np.zeros((len(cu) - 1,) + q.shape[1:], dtype=q.dtype)
+    for s in range(len(cu) - 1):
+        if cu[s + 1] > cu[s]:
+            out[s] = q[cu[s + 1] - 1]
+    return out
