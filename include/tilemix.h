@@ -148,6 +148,44 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
                            const int8_t* k_i8, const float* q_scale, const float* k_scale,
                            const uint64_t* words_d, void* out_f16, void* hip_stream);
 
+/* INT8 key/value cache quantiser (device) -- [Explainer, 支持的场景]; [Digest,
+ * setup]: the decode side keeps the cache in INT8.  Both K and V use the
+ * prefill quantiser's key blocks: per (head, 64-row block of one sequence),
+ * a = max|x|, s = a / 127, q = round-half-even(x / s) clamped to [-127, 127],
+ * both divisions IEEE binary32, a = 0 gives s = 0 and q = 0.  The plan is the
+ * one of the cache lengths.
+ * Inputs:  k_f16, v_f16 [T, Hkv, d] (device).
+ * Outputs: k_i8, v_i8 [T, Hkv, d] (device int8); k_scale, v_scale
+ *          float[Hkv][total_k_tiles] (device). */
+int tilemix_quantize_kv(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16,
+                        const void* v_f16, int8_t* k_i8, int8_t* v_i8, float* k_scale,
+                        float* v_scale, void* hip_stream);
+
+/* Bytes of device workspace tilemix_decode_varlen needs for this plan:
+ * B * Hq * ceil(max L / 256) * (d + 2) * 4. */
+int tilemix_decode_workspace_size(const int32_t* plan_h, int64_t* bytes);
+
+/* One decode step against the INT8 cache (device).  The plan and routing
+ * words are those of the cache lengths L_s (cu_seqlens of the cache, which
+ * already holds the new tokens).  Each sequence's new query is the token at
+ * position L_s - 1; it attends to all L_s cached positions.  Key tile t of
+ * sequence s is routed by bit t / g of the word of the query-tile row holding
+ * L_s - 1 ([Map, hot loop]):
+ *   bit 1: S = float(int32 sum of q_i8 * k_i8) * (s_q * s_k / sqrt(d)), with
+ *          q_i8, s_q the query quantised on its own (a block of one row);
+ *   bit 0: S = (fp16 q . (k_i8 * s_k)) / sqrt(d);
+ * then softmax over the L_s keys with P rounded to fp16 and
+ * O = sum P (v_i8 * s_v) / sum P, written as fp16.
+ * q_f16: device [B, Hq, d]; k_i8, v_i8, k_scale, v_scale from
+ * tilemix_quantize_kv; words_d from tilemix_build_routing; workspace: device
+ * scratch of at least tilemix_decode_workspace_size bytes (its contents are
+ * overwritten); out_f16: device [B, Hq, d] (zeros for an empty sequence).
+ * Errors: EINVAL for a missing or misaligned pointer or a small workspace. */
+int tilemix_decode_varlen(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                          const int8_t* k_i8, const int8_t* v_i8, const float* k_scale,
+                          const float* v_scale, const uint64_t* words_d, void* workspace,
+                          int64_t workspace_bytes, void* out_f16, void* hip_stream);
+
 /* Test hook (device): the int32 accumulator of one 128 x 64 INT8 score tile
  * (sequence seq, query head, query-tile row r, key tile t), computed by the
  * same device routine the fused kernel uses ([Digest, method]: INT8 MMA with

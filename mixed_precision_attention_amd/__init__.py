@@ -5,7 +5,8 @@ quantisation, fused attention) runs inside libtilemix.so -- the host steps in
 its C++ half, the device steps in its HIP kernels.  PyTorch supplies device
 memory and the current HIP stream.  The functions carry the names of the C
 entry points declared in include/tilemix.h; ``TileMixPrefill`` bundles them
-for one packed batch shape.
+for one packed batch shape and ``TileMixDecode`` for one decode step over an
+INT8 key/value cache.
 
 The library must be built first (``python -m mixed_precision_attention_amd.build``);
 importing works without it, but every call raises ``TileMixError`` when the
@@ -53,6 +54,9 @@ _SIGNATURES = {
     "tilemix_quantize_qk": ([_P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "tilemix_prefill_varlen": ([_P] * 12, ctypes.c_int),
     "tilemix_debug_qk_i32_tile": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
+    "tilemix_quantize_kv": ([_P] * 9, ctypes.c_int),
+    "tilemix_decode_workspace_size": ([_P, _P], ctypes.c_int),
+    "tilemix_decode_varlen": ([_P] * 9 + [_I64, _P, _P], ctypes.c_int),
 }
 
 
@@ -176,6 +180,33 @@ def tilemix_debug_qk_i32_tile(plan_h, plan_d, q_i8, k_i8, seq: int, head: int, r
         _stream(stream)))
 
 
+def tilemix_quantize_kv(plan_h, plan_d, k, v, k_i8, v_i8, k_scale, v_scale, stream=None):
+    import torch
+    _check(lib().tilemix_quantize_kv(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(k, torch.float16, "k"),
+        _dptr(v, torch.float16, "v"), _dptr(k_i8, torch.int8, "k_i8"), _dptr(v_i8, torch.int8, "v_i8"),
+        _dptr(k_scale, torch.float32, "k_scale"), _dptr(v_scale, torch.float32, "v_scale"),
+        _stream(stream)))
+
+
+def tilemix_decode_workspace_size(plan_h) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().tilemix_decode_workspace_size(_hptr(plan_h), ctypes.byref(n)))
+    return int(n.value)
+
+
+def tilemix_decode_varlen(plan_h, plan_d, q, k_i8, v_i8, k_scale, v_scale, words_d, workspace, out,
+                          stream=None):
+    import torch
+    _check(lib().tilemix_decode_varlen(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
+        _dptr(k_i8, torch.int8, "k_i8"), _dptr(v_i8, torch.int8, "v_i8"),
+        _dptr(k_scale, torch.float32, "k_scale"), _dptr(v_scale, torch.float32, "v_scale"),
+        _dptr(words_d, torch.int64, "words_d"), _dptr(workspace, torch.uint8, "workspace"),
+        workspace.numel() if workspace is not None else 0, _dptr(out, torch.float16, "out"),
+        _stream(stream)))
+
+
 # ------------------------------------------------------------------ bundle
 
 class TileMixPrefill:
@@ -220,4 +251,46 @@ class TileMixPrefill:
             out = torch.empty_like(q)
         self.quantize(q, k, stream)
         self.attend(q, k, v, out, stream)
+        return out
+
+
+class TileMixDecode:
+    """One decode step's shape over an INT8 key/value cache: the plan and
+    routing words of the cache lengths, the int8 cache with its scales, and
+    the workspace of the split-key merge."""
+
+    def __init__(self, cu_seqlens, hq: int, hkv: int, head_dim: int, template, coverage_bp: int,
+                 seed: int = 0, device="cuda"):
+        import torch
+        self.cu = _host_i32(cu_seqlens)
+        self.batch = len(self.cu) - 1
+        self.hq, self.hkv, self.d = hq, hkv, head_dim
+        self.tokens, self.tq, self.tk = tilemix_query_sizes(self.cu)
+        self.plan_h = tilemix_build_plan(self.cu, hq, hkv, head_dim)
+        self.plan_d = torch.from_numpy(self.plan_h).to(device)
+        self.device = device
+        self.words, self.g, self.n_int8, self.n_legal = tilemix_build_routing(
+            self.cu, hkv, template, coverage_bp, seed)
+        w = self.words if self.words.size else np.zeros((1, 1), dtype=np.uint64)
+        self.words_d = torch.from_numpy(w.view(np.int64)).to(device)
+        t = max(self.tokens, 1)
+        self.k_i8 = torch.empty((t, hkv, head_dim), dtype=torch.int8, device=device)
+        self.v_i8 = torch.empty((t, hkv, head_dim), dtype=torch.int8, device=device)
+        self.k_scale = torch.empty((hkv, max(self.tk, 1)), dtype=torch.float32, device=device)
+        self.v_scale = torch.empty((hkv, max(self.tk, 1)), dtype=torch.float32, device=device)
+        self.workspace = torch.empty(max(tilemix_decode_workspace_size(self.plan_h), 16),
+                                     dtype=torch.uint8, device=device)
+
+    def fill_cache(self, k, v, stream=None):
+        """Quantise fp16 K, V [T, Hkv, d] into the INT8 cache."""
+        tilemix_quantize_kv(self.plan_h, self.plan_d, k, v, self.k_i8, self.v_i8, self.k_scale,
+                            self.v_scale, stream)
+
+    def step(self, q, out=None, stream=None):
+        """q: fp16 [B, Hq, d], the newest query of each sequence."""
+        import torch
+        if out is None:
+            out = torch.empty((self.batch, self.hq, self.d), dtype=torch.float16, device=q.device)
+        tilemix_decode_varlen(self.plan_h, self.plan_d, q, self.k_i8, self.v_i8, self.k_scale,
+                              self.v_scale, self.words_d, self.workspace, out, stream)
         return out

@@ -142,6 +142,27 @@ def test_errors_are_reported():
                                    None) == -2
 
 
+def test_decode_host_checks():
+    cu = synth.cu_seqlens_of([300, 0, 4096])
+    plan = tm.tilemix_build_plan(cu, 6, 2, 128)
+    # B * Hq * ceil(max L / 256) * (d + 2) * 4 bytes
+    assert tm.tilemix_decode_workspace_size(plan) == 3 * 6 * 16 * 130 * 4
+    lib = tm.lib()
+    p = ctypes.c_void_p(plan.ctypes.data)
+    fake = ctypes.c_void_p(16)
+    args = [p, fake, fake, fake, fake, fake, fake, fake, fake]
+    assert lib.tilemix_decode_varlen(*args, 100, fake, None) == -1
+    assert "workspace" in tm.tilemix_last_error()
+    assert lib.tilemix_decode_varlen(p, fake, ctypes.c_void_p(24), *args[3:], 1 << 20, fake, None) == -1
+    assert "aligned" in tm.tilemix_last_error()
+    assert lib.tilemix_quantize_kv(p, fake, None, fake, fake, fake, fake, fake, None) == -1
+    assert "k_f16" in tm.tilemix_last_error()
+    empty = tm.tilemix_build_plan(np.array([0], dtype=np.int32), 2, 2, 64)
+    pe = ctypes.c_void_p(empty.ctypes.data)
+    assert tm.tilemix_decode_workspace_size(empty) == 0
+    assert lib.tilemix_decode_varlen(pe, fake, None, None, None, None, None, None, None, 0, None, None) == 0
+
+
 def test_empty_batch_is_a_no_op():
     cu = np.array([0, 0], dtype=np.int32)
     w, g, n8, nl = tm.tilemix_build_routing(cu, 2, "band", 5000)
