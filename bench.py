@@ -14,6 +14,11 @@ resident in HBM.  ``roofline`` refers to the fused prefill kernel: achieved
 fp16-equivalent TFLOP/s (INT8 operations weighted by the fp16/int8 peak
 ratio) against the published MI355X dense fp16 MFMA peak, i.e. ``frac`` is
 the coverage-weighted MFMA roofline time over the measured kernel time.
+
+``decode`` (skip with --no-decode) times one decode step per sequence against
+an INT8 key/value cache holding the same workload's K and V: tokens/s is new
+tokens per second, and its roofline is HBM bandwidth over the step's
+algorithmic bytes.
 """
 
 from __future__ import annotations
@@ -30,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16 = 2.5e15   # MI355X dense fp16 MFMA, FLOP/s (published)
 PEAK_I8 = 5.0e15    # MI355X dense int8 MFMA, OP/s (published)
+PEAK_HBM = 8.0e12   # MI355X HBM3E, bytes/s (published)
 METRIC = "prefill attn tokens/s + % of MFMA roofline, 3B shape L=4k B=8 SpTrans75"
 KERNEL_SRC = os.path.join(ROOT, "mixed_precision_attention_amd", "csrc", "tilemix_kernels.hip")
 
@@ -113,17 +119,91 @@ def write_traffic(args):
     return 0
 
 
+def decode_bytes(cu, hq, hkv, d, tq, tk):
+    """Algorithmic HBM bytes of one decode step: the INT8 cache (K and V) and
+    its scales read once, the routing words, the queries read and the output
+    written once, and the split-key workspace written and read once."""
+    import numpy as np
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    tokens = int(lens.sum())
+    chunks = int(sum(-(-int(L) // 256) for L in lens))
+    B = len(lens)
+    return (2 * tokens * hkv * d + 2 * hkv * tk * 4 + hkv * tq * 8 + 2 * B * hq * d * 2
+            + 2 * B * hq * chunks * (d + 2) * 4)
+
+
+def bench_decode(q, k, v, cu, spec, template, coverage, steps, warmup, cpu):
+    """One decode step per sequence against the INT8 cache of the workload's
+    K and V (the newest token of each sequence is the query)."""
+    import numpy as np
+    import torch
+    import mixed_precision_attention_amd as tm
+    import synth
+    hq, hkv, d = spec["hq"], spec["hkv"], spec["d"]
+    td = tm.TileMixDecode(cu, hq, hkv, d, template, coverage)
+    kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    q_new = synth.decode_queries(q, cu)
+    qd = torch.from_numpy(q_new).cuda()
+    td.fill_cache(kd, vd)
+    out = torch.empty((len(cu) - 1, hq, d), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        td.step(qd, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        td.step(qd, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = decode_bytes(cu, hq, hkv, d, td.tq, td.tk)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    rec = {
+        "metric": "decode tokens/s (one new token per sequence, INT8 key/value cache)",
+        "value": (len(cu) - 1) / (us * 1e-6), "unit": "tokens/s", "us_per_step": us,
+        "steps": steps, "warmup": warmup,
+        "config": {"workload": f"decode_{spec['name']}_{template}{coverage // 100}",
+                   "cache_lengths": f"{len(cu) - 1}x{int(cu[1] - cu[0])}"
+                   if len(set(np.diff(cu))) == 1 else np.diff(cu).tolist(),
+                   "hq": hq, "hkv": hkv, "head_dim": d},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": achieved * 1e9 / PEAK_HBM, "traffic": None,
+                     "algorithmic_bytes": nbytes, "launches": "decode_partial + decode_merge"},
+    }
+    if cpu:
+        import oracle
+        t0 = time.perf_counter()
+        k_i8, ks, v_i8, vs = oracle.quantize_kv_cache(k, v, cu)
+        t_q = time.perf_counter() - t0
+        n = min(2, len(cu) - 1)
+        sub = np.asarray(cu[:n + 1])
+        t1 = time.perf_counter()
+        oracle.decode_attention(q_new[:n], k_i8[:sub[-1]], ks, v_i8[:sub[-1]], vs, td.words, sub, hq, hkv)
+        t_d = (time.perf_counter() - t1) * int(cu[-1]) / int(sub[-1])
+        rec["cpu_baseline"] = {"value": (len(cu) - 1) / t_d, "unit": "tokens/s", "cores": _blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"decode of the first {n} sequences ({int(sub[-1])} cached "
+                                         f"tokens), extrapolated by cached tokens; the cache "
+                                         f"quantiser ({t_q:.1f}s) is outside the step"}
+    return rec
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(q, k, v, cu, spec, template, coverage, budget_s=20.0):
     """The oracle, as it stands, on a bounded sample of the workload: the
     full quantiser pass plus sampled work units of the attention,
     extrapolated to the whole batch by legal-pair count."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = _blas_threads()
     t0 = time.perf_counter()
     words, g, n8, nl = oracle.routing_words(np.diff(cu).tolist(), spec["hkv"], template, coverage, 0)
     q_i8, q_s = oracle.quantize_blocks(q, cu, oracle.BLOCK_M)
@@ -165,6 +245,9 @@ def main(argv=None):
     ap.add_argument("--template", default=None)
     ap.add_argument("--coverage", type=int, default=None, help="INT8 coverage in basis points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode step over the INT8 key/value cache")
+    ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
@@ -285,6 +368,10 @@ def main(argv=None):
                       "roofline_us": t_roof * 1e6, "host_build_ms": host_build_ms,
                       "wall_s": wall},
     }
+    if not args.no_decode:
+        spec_named = dict(spec, name=args.workload)
+        result["decode"] = bench_decode(q, k, v, cu, spec_named, template, coverage, args.decode_steps,
+                                        20, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, cu, spec, template, coverage, args.cpu_budget)
     else:

@@ -133,22 +133,18 @@ struct DecodeArgs {
   const uint64_t* words; // [Hkv, tq]
   float* work;           // [B, Hq, chunks, D + 2]
   _Float16* out;         // [B, Hq, D]
-  int32_t hq, hkv, tq, tk, chunks, head_groups;
+  int32_t batch, hq, hkv, tq, tk, chunks, head_groups;
 };
 
 template <int D>
 struct Smem {
-  static constexpr int kVPitch = D + 16;            // bytes per staged value row
   _Float16 qf[kMaxG][D];                            // fp16 queries
   int8_t qi[kMaxG][D];                              // int8 queries
   float sq[kMaxG];                                  // query scales
   float mx[4][kMaxG];                               // per-wave maxima
   float ls[4][kMaxG];                               // per-wave sums of P
-  float pv[kMaxG][kChunk];                          // fp16-rounded P times s_v
-  union {
-    int8_t v[kChunk][kVPitch];                      // staged int8 values
-    float part[kThreads / (D / 4)][kMaxG][D];       // per-part P.V sums
-  } u;
+  _Float16 pv[kMaxG][kChunk];                       // fp16-rounded P
+  float part[4][kMaxG][D];                          // per-wave P.V sums
 };
 
 // Signed int8 x4 -> two fp16 pairs, exactly: bytes b + 128 become the low
@@ -176,55 +172,20 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
 
-  // Queries of the group: fp16 copy, and the int8 copy with one scale per
-  // (sequence, head) -- the quantiser with a block of one row.
-  for (int h = w; h < G; h += 4) {
-    const _Float16* qrow = a.q + ((size_t)seq * a.hq + h0 + h) * D;
-    float x[D / 64];
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
-      const _Float16 hv = qrow[lane + 64 * i];
-      sm.qf[h][lane + 64 * i] = hv;
-      x[i] = (float)hv;
-      amax = fmaxf(amax, fabsf(x[i]));
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const float sq = __fdiv_rn(amax, 127.0f);
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
-      const float qv = amax > 0.f ? __builtin_rintf(__fdiv_rn(x[i], sq)) : 0.f;
-      sm.qi[h][lane + 64 * i] = (int8_t)(int)__builtin_amdgcn_fmed3f(qv, -127.f, 127.f);
-    }
-    if (lane == 0) sm.sq[h] = sq;
-  }
-
-  // Stage the chunk's int8 values (rows past the sequence end as zeros).
-  {
-    constexpr int kPerRow = D / 16;
-#pragma unroll
-    for (int i = 0; i < kChunk * kPerRow / kThreads; ++i) {
-      const int idx = tid + i * kThreads, r = idx / kPerRow, cc = idx % kPerRow;
-      const int j = chunk * kChunk + r;
-      int4v x = {0, 0, 0, 0};
-      if (j < L) x = *reinterpret_cast<const int4v*>(a.vi8 + ((size_t)(start + j) * a.hkv + kv) * D + cc * 16);
-      *reinterpret_cast<int4v*>(&sm.u.v[r][cc * 16]) = x;
-    }
-  }
-  __syncthreads();
-
-  // Scores of this wave's key tile, one key per lane, in the log2 domain.
-  const int t = chunk * 4 + w;              // key tile (sequence-local)
-  const int j = t * kBlockN + lane;         // key
+  // Every load of the workgroup is issued up front -- the queries first, then
+  // this lane's key row and this thread's share of the staged values -- so
+  // their latencies overlap.
+  const int t = chunk * 4 + w;              // this wave's key tile (sequence-local)
+  const int j = t * kBlockN + lane;         // this lane's key
   const bool live = j < L;
-  const int kt = rec[kSeqKtOff] + t;
-  const int g = rec[kSeqG];
-  const int r = (L - 1) / kBlockM;
-  const uint64_t word = a.words[(size_t)kv * a.tq + rec[kSeqQtOff] + r];
-  const bool bit = t * kBlockN < L && ((word >> (t / g)) & 1ull);
-  const float s_k = t * kBlockN < L ? a.ks[(size_t)kv * a.tk + kt] : 0.f;
-  const float s_v = t * kBlockN < L ? a.vs[(size_t)kv * a.tk + kt] : 0.f;
+  const bool tile_live = t * kBlockN < L;
+  _Float16 qv[2][D / 64];                   // heads w and w + 4 of the group
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i)
+      qv[u][i] = w + 4 * u < G ? a.q[((size_t)seq * a.hq + h0 + w + 4 * u) * D + lane + 64 * i]
+                               : (_Float16)0.0f;
   uint32_t kw[D / 4] = {};
   if (live) {
     const int4v* krow = reinterpret_cast<const int4v*>(a.ki8 + ((size_t)(start + j) * a.hkv + kv) * D);
@@ -234,6 +195,51 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
       kw[4 * i] = x[0]; kw[4 * i + 1] = x[1]; kw[4 * i + 2] = x[2]; kw[4 * i + 3] = x[3];
     }
   }
+  // Values in the P.V layout: thread (4 channels c4, key part) holds its 4
+  // channels of each of its keys (a wave reads whole 128-byte rows).
+  constexpr int kGroups = D / 4, kParts = kThreads / kGroups, kKeys = kChunk / kParts;
+  const int c4 = tid % kGroups, part = tid / kGroups;
+  uint32_t vreg[kKeys];
+#pragma unroll
+  for (int k = 0; k < kKeys; ++k) {
+    const int jj = chunk * kChunk + part * kKeys + k;
+    vreg[k] = jj < L ? *reinterpret_cast<const uint32_t*>(a.vi8 + ((size_t)(start + jj) * a.hkv + kv) * D + c4 * 4)
+                     : 0u;
+  }
+  const int vt = chunk * 4 + part * kKeys / kBlockN;  // key tile of this part
+  const float s_vp = vt * kBlockN < L ? a.vs[(size_t)kv * a.tk + rec[kSeqKtOff] + vt] : 0.f;
+  const int kt = rec[kSeqKtOff] + t;
+  const float s_k = tile_live ? a.ks[(size_t)kv * a.tk + kt] : 0.f;
+  const uint64_t word = a.words[(size_t)kv * a.tq + rec[kSeqQtOff] + (L - 1) / kBlockM];
+  const bool bit = tile_live && ((word >> (t / rec[kSeqG])) & 1ull);
+
+  // Queries of the group: fp16 copy, and the int8 copy with one scale per
+  // (sequence, head) -- the quantiser with a block of one row.
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int h = w + 4 * u;
+    if (h >= G) break;
+    float x[D / 64];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      sm.qf[h][lane + 64 * i] = qv[u][i];
+      x[i] = (float)qv[u][i];
+      amax = fmaxf(amax, fabsf(x[i]));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float sq = __fdiv_rn(amax, 127.0f);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const float qq = amax > 0.f ? __builtin_rintf(__fdiv_rn(x[i], sq)) : 0.f;
+      sm.qi[h][lane + 64 * i] = (int8_t)(int)__builtin_amdgcn_fmed3f(qq, -127.f, 127.f);
+    }
+    if (lane == 0) sm.sq[h] = sq;
+  }
+  __syncthreads();
+
+  // Scores of this wave's key tile, one key per lane, in the log2 domain.
   float xs[kMaxG];
   if (bit) {
 #pragma unroll
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
     const float m = fmaxf(fmaxf(sm.mx[0][h], sm.mx[1][h]), fmaxf(sm.mx[2][h], sm.mx[3][h]));
     // P rounded to fp16; the normaliser sums the same rounded values
     const float p = live ? (float)(_Float16)__builtin_amdgcn_exp2f(xs[h] - m) : 0.f;
-    sm.pv[h][w * kBlockN + lane] = p * s_v;
+    sm.pv[h][w * kBlockN + lane] = (_Float16)p;
     float l = p;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
@@ -287,33 +293,38 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
   }
   __syncthreads();
 
-  // P.V with the dequantised values: thread (4 channels, key part) sums its
-  // keys; s_v is folded into pv[].
-  constexpr int kGroups = D / 4, kParts = kThreads / kGroups, kKeys = kChunk / kParts;
-  const int c4 = tid % kGroups, part = tid / kGroups;
+  // P.V with the dequantised values: each thread sums its keys two at a time
+  // with fp16 pair dot products (fp16 P and int8 values are exact in fp16;
+  // products exact, fp32 sums), then applies its key tile's value scale (a
+  // part lies inside one key tile).
   float acc[kMaxG][4] = {};
-#pragma unroll 4
-  for (int k = 0; k < kKeys; ++k) {
+#pragma unroll
+  for (int k = 0; k < kKeys; k += 2) {
     const int key = part * kKeys + k;
-    const uint32_t vw = *reinterpret_cast<const uint32_t*>(&sm.u.v[key][c4 * 4]);
-    const float v0 = (float)(int8_t)(vw & 0xff), v1 = (float)(int8_t)((vw >> 8) & 0xff);
-    const float v2 = (float)(int8_t)((vw >> 16) & 0xff), v3 = (float)(int8_t)(vw >> 24);
+    // (channel c of key, of key + 1) pairs for the 4 channels
+    half2v v01[4];
+    i8x4_to_half(__builtin_amdgcn_perm(vreg[k + 1], vreg[k], 0x05010400u), v01[0], v01[1]);
+    i8x4_to_half(__builtin_amdgcn_perm(vreg[k + 1], vreg[k], 0x07030602u), v01[2], v01[3]);
 #pragma unroll
     for (int h = 0; h < kMaxG; ++h) {
       if (h >= G) break;
-      const float p = sm.pv[h][key];
-      acc[h][0] += p * v0;
-      acc[h][1] += p * v1;
-      acc[h][2] += p * v2;
-      acc[h][3] += p * v3;
+      const half2v pp = *reinterpret_cast<const half2v*>(&sm.pv[h][key]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[h][e] = __builtin_amdgcn_fdot2(pp, v01[e], acc[h][e], false);
     }
   }
-  __syncthreads();  // done with the staged values: the union becomes part[]
+  // Sum the parts: lanes l, l + kGroups, ... of a wave hold the same
+  // channels, then the four waves through LDS.
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     if (h >= G) break;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.u.part[part][h][c4 * 4 + e] = acc[h][e];
+    for (int e = 0; e < 4; ++e) {
+      float x = acc[h][e] * s_vp;
+#pragma unroll
+      for (int off = kGroups; off < 64; off <<= 1) x += __shfl_xor(x, off);
+      if (lane < kGroups) sm.part[w][h][c4 * 4 + e] = x;
+    }
   }
   __syncthreads();
   // Workspace record of (sequence, head, chunk): m, l, O[D] (unnormalised).
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
     const int h = idx / D, c = idx % D;
     float o = 0.f;
 #pragma unroll
-    for (int p = 0; p < kParts; ++p) o += sm.u.part[p][h][c];
+    for (int p = 0; p < 4; ++p) o += sm.part[p][h][c];
     float* rec_out = a.work + (((size_t)seq * a.hq + h0 + h) * a.chunks + chunk) * (D + 2);
     rec_out[2 + c] = o;
     if (c == 0) {
@@ -331,31 +342,46 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
   }
 }
 
-// Merge of the chunks of one (sequence, query head): the online-softmax
-// combination of partial states ([Routes, precision routing]: one shared
-// state), O = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i, written as fp16.
+// Merge of the chunks of one (sequence, query head), one wave each: the
+// online-softmax combination of partial states ([Routes, precision routing]:
+// one shared state), O = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i, written
+// as fp16.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
-  const int seq = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
+  const int wid = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wid >= a.batch * a.hq) return;
+  const int seq = wid / a.hq, h = wid % a.hq;
   const int L = a.plan[kHeaderLen + seq * kSeqStride + kSeqLen];
-  const int c = threadIdx.x;
   _Float16* o = a.out + ((size_t)seq * a.hq + h) * D;
   if (L == 0) {
-    o[c] = (_Float16)0.0f;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) o[lane + 64 * i] = (_Float16)0.0f;
     return;
   }
   const int n = (L + kChunk - 1) / kChunk;
   const float* base = a.work + ((size_t)seq * a.hq + h) * a.chunks * (D + 2);
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, base[(size_t)i * (D + 2)]);
-  float l = 0.f, acc = 0.f;
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, base[(size_t)i * (D + 2)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float l = 0.f;
+  for (int i = lane; i < n; i += 64) {
+    const float* r = base + (size_t)i * (D + 2);
+    l += __builtin_amdgcn_exp2f(r[0] - M) * r[1];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+  float acc[D / 64] = {};
+#pragma unroll 4
   for (int i = 0; i < n; ++i) {
     const float* r = base + (size_t)i * (D + 2);
     const float wgt = __builtin_amdgcn_exp2f(r[0] - M);
-    l += wgt * r[1];
-    acc += wgt * r[2 + c];
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) acc[c] += wgt * r[2 + lane + 64 * c];
   }
-  o[c] = (_Float16)(acc / l);
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) o[lane + 64 * c] = (_Float16)(acc[c] * inv);
 }
 
 }  // namespace decode
@@ -468,6 +494,7 @@ int tilemix_decode_varlen(const int32_t* plan_h, const int32_t* plan_d, const vo
   a.words = words_d;
   a.work = static_cast<float*>(workspace);
   a.out = static_cast<_Float16*>(out_f16);
+  a.batch = batch;
   a.hq = plan_h[kHq];
   a.hkv = plan_h[kHkv];
   a.tq = plan_h[kTotalQTiles];
@@ -487,11 +514,11 @@ int tilemix_decode_varlen(const int32_t* plan_h, const int32_t* plan_d, const vo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
-  const unsigned merge = (unsigned)((int64_t)batch * a.hq);
+  const unsigned merge = (unsigned)(((int64_t)batch * a.hq + 3) / 4);  // one wave per (sequence, head)
   if (d == 64)
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(merge), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(merge), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(merge), dim3(128), 0, st, a);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(merge), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode merge launch");
   return TILEMIX_OK;
