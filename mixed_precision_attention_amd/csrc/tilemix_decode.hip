@@ -157,7 +157,7 @@ __device__ inline void i8x4_to_half(uint32_t w, half2v& lo, half2v& hi) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs a) {
   __shared__ Smem<D> sm;
   const int chunk = blockIdx.x;
   const int hg = blockIdx.y % a.head_groups;
