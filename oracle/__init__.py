@@ -6,4 +6,5 @@ from .tilemix_oracle import (BLOCK_M, BLOCK_N, TEMPLATES, SeqGeometry, seq_geome
                              quantize_blocks, qk_int32_tile, prefill_attention, run,
                              splitmix64_mix, rowrandom_hash, sptrans_stride, union_orders,
                              softmax_scale, int8_tile_scale, quantize_kv_cache,
-                             quantize_query_rows, decode_attention)
+                             quantize_query_rows, decode_attention, block_column_sums,
+                             routing_importance, adaptive_words, importance_exposure)

@@ -552,3 +552,143 @@ def decode_attention(q, k_i8, k_scale, v_i8, v_scale, words, cu_seqlens, hq: int
                 p = p.astype(np.float16).astype(np.float64)
             out[s, h, :] = (p @ vhat) / p.sum()
     return out
+
+
+# ---------------------------------------------------------------------------
+# Adaptive routing words from a per-tile statistic, and the importance probe
+# ---------------------------------------------------------------------------
+#
+# [Digest, setup] and [Routes, "The A100 result should not be exported
+# unchanged"]: the evaluated routing is static and data-free; the interface
+# accepts adaptive policies, which the pages leave untested.  [Explainer,
+# 体检] / [Routes, "Placement can matter more than the nominal percentage"]:
+# the pages probe a layout by the share of high-importance attention mass
+# that lands in INT8 groups (about 8.5% for SpTrans at 25%).  Readings taken
+# here (a cheap statistic from data the quantiser already produced):
+#   * per block, the column sums of its int8 codes (Q: 128-row blocks per
+#     query head; K: 64-row tiles per KV head);
+#   * pooled score of (query head h, row r, key tile t):
+#     z = fl32(dot) * fl32(fl32(s_q * s_k) / (n_q * n_k)), dot the exact
+#     integer dot product of the two column-sum vectors and n_q, n_k the rows
+#     of the blocks -- the mean query of the block against the mean key of
+#     the tile, in binary32 with this order of operations;
+#   * Z(kv, r, t) = max over the query heads of the KV head;
+#   * importance of group (r, G) = max of Z over its legal tiles minus the
+#     max of Z over the row's legal tiles (binary32; 0 for the row's best
+#     group, negative otherwise);
+#   * per (sequence, KV head) the legal groups are ordered by (importance, r,
+#     G) ascending and the first N8 (the same count as a static template at
+#     that coverage) go INT8: the groups farthest below their row's strongest
+#     group lose precision first.
+
+
+def block_column_sums(x_i8, cu_seqlens, block: int):
+    """Column sums of the int8 codes of each (head, block): int64
+    [H, tiles, d], tiles numbered per sequence and concatenated."""
+    cu = [int(c) for c in cu_seqlens]
+    T, H, d = x_i8.shape
+    sums, rows = [], []
+    for s in range(len(cu) - 1):
+        for b0 in range(cu[s], cu[s + 1], block):
+            b1 = min(b0 + block, cu[s + 1])
+            sums.append(x_i8[b0:b1].astype(np.int64).sum(axis=0))   # [H, d]
+            rows.append(b1 - b0)
+    if not sums:
+        return np.zeros((H, 0, d), dtype=np.int64), np.zeros(0, dtype=np.int64)
+    return np.stack(sums, axis=1), np.array(rows, dtype=np.int64)
+
+
+def routing_importance(q_i8, k_i8, q_scale, k_scale, cu_seqlens, hq: int, hkv: int):
+    """Importance of every legal group, float32 [Hkv, sum Tm, 64]; +inf for
+    the slots of illegal groups."""
+    cu = [int(c) for c in cu_seqlens]
+    seqlens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    grp = hq // hkv
+    qs, qrows = block_column_sums(q_i8, cu, BLOCK_M)
+    ks, krows = block_column_sums(k_i8, cu, BLOCK_N)
+    qt_off, kt_off = _tile_offsets(seqlens)
+    out = np.full((hkv, qt_off[-1], WORD_BITS), np.inf, dtype=np.float32)
+    for s, L in enumerate(seqlens):
+        geo = seq_geometry(L)
+        for r in range(geo.Tm):
+            qt = qt_off[s] + r
+            nt = geo.last_tile[r] + 1
+            for kv in range(hkv):
+                Z = np.full(nt, -np.inf, dtype=np.float32)
+                for h in range(kv * grp, kv * grp + grp):
+                    for t in range(nt):
+                        kt = kt_off[s] + t
+                        dot = int(qs[h, qt] @ ks[kv, kt])
+                        a = np.float32(q_scale[h, qt] * k_scale[kv, kt])
+                        b = np.float32(a / np.float32(qrows[qt] * krows[kt]))
+                        z = np.float32(np.float32(dot) * b)
+                        Z[t] = max(Z[t], z)
+                zrow = Z.max()
+                for G in range(geo.D[r] + 1):
+                    zg = Z[G * geo.g:min(G * geo.g + geo.g, nt)].max()
+                    out[kv, qt, G] = np.float32(zg - zrow)
+    return out
+
+
+def adaptive_words(seqlens, importance, coverage_bp: int):
+    """Routing words from group importances: per (sequence, KV head), the N8
+    legal groups first in (importance, r, G) order are INT8.  Returns (words
+    uint64 [Hkv, sum Tm], g int32 [B], N8 int64 [B], N_legal int64 [B])."""
+    hkv = importance.shape[0]
+    geos = [seq_geometry(int(L)) for L in seqlens]
+    total_tm = sum(geo.Tm for geo in geos)
+    words = np.zeros((hkv, total_tm), dtype=np.uint64)
+    gs, n8s, nls = [], [], []
+    off = 0
+    for geo in geos:
+        n8 = int8_group_count(coverage_bp, geo.n_legal)
+        for kv in range(hkv):
+            order = sorted(geo.legal_groups(), key=lambda rg: (importance[kv, off + rg[0], rg[1]], rg[0], rg[1]))
+            for (r, G) in order[:n8]:
+                words[kv, off + r] |= np.uint64(1 << G)
+        gs.append(geo.g)
+        n8s.append(n8)
+        nls.append(geo.n_legal)
+        off += geo.Tm
+    return words, np.array(gs, dtype=np.int32), np.array(n8s, dtype=np.int64), np.array(nls, dtype=np.int64)
+
+
+def importance_exposure(q, k, cu_seqlens, hq: int, hkv: int, words, tau: float = 0.5, heads=None):
+    """Share of high-importance attention mass that a layout routes to INT8.
+
+    Importance is the attention probability of the exact (fp64) causal
+    softmax of the fp16 inputs.  Per query row, the high-importance pairs are
+    the fewest keys whose probabilities reach a share ``tau`` of the row's
+    mass; the result is their mass inside INT8 groups over their whole mass,
+    summed over rows (and the given query heads).
+    """
+    cu = [int(c) for c in cu_seqlens]
+    grp = hq // hkv
+    qt_off, _ = _tile_offsets([cu[i + 1] - cu[i] for i in range(len(cu) - 1)])
+    heads = range(hq) if heads is None else heads
+    inside = total = 0.0
+    for s in range(len(cu) - 1):
+        start, L = cu[s], cu[s + 1] - cu[s]
+        if L == 0:
+            continue
+        geo = seq_geometry(L)
+        for h in heads:
+            kv = h // grp
+            qf = q[start:start + L, h, :].astype(np.float64)
+            kf = k[start:start + L, kv, :].astype(np.float64)
+            S = qf @ kf.T / math.sqrt(q.shape[2])
+            S[np.triu_indices(L, 1)] = -np.inf
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            for i in range(L):
+                p = P[i, :i + 1]
+                order = np.argsort(-p, kind="stable")
+                cum = np.cumsum(p[order])
+                n = int(np.searchsorted(cum, tau) + 1)
+                sel = order[:n]
+                r = i // BLOCK_M
+                word = np.uint64(words[kv, qt_off[s] + r])
+                bits = (word >> ((sel // BLOCK_N) // geo.g).astype(np.uint64)) & np.uint64(1)
+                inside += float(p[sel][bits == 1].sum())
+                total += float(p[sel].sum())
+    return inside / total if total else 0.0

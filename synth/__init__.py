@@ -121,3 +121,34 @@ def decode_queries(q, cu_seqlens):
         if cu[s + 1] > cu[s]:
             out[s] = q[cu[s + 1] - 1]
     return out
+
+
+def make_qkv_local(seqlens, hq: int, hkv: int, d: int, seed: int = 0, amp: float = 1.5,
+                   sink: float = 8.0):
+    """Inputs whose attention has the structure real layers show: locality
+    and a sink.  Q, K, V are drawn as in ``make_qkv`` (no outlier channels);
+    then, per sequence-local position i, channels 2c, 2c+1 (c < 16) of Q and K
+    gain amp * (cos, sin)(w_c i) with periods 32 * 2^(c/2) tokens, so q_i . k_j
+    grows as |i - j| shrinks, and channel 32 gains 2 in every query and
+    ``sink`` in each sequence's first key.  Rounded to float16."""
+    cu = cu_seqlens_of(seqlens)
+    rng = np.random.default_rng(seed)
+    t = int(cu[-1])
+    q = rng.standard_normal((t, hq, d), dtype=np.float32)
+    k = rng.standard_normal((t, hkv, d), dtype=np.float32)
+    v = rng.standard_normal((t, hkv, d), dtype=np.float32)
+    pos = np.concatenate([np.arange(int(cu[s + 1] - cu[s])) for s in range(len(seqlens))]
+                         + [np.zeros(0)]).astype(np.float64)
+    for c in range(16):
+        w = 2.0 * np.pi / (32.0 * 2.0 ** (c / 2.0))
+        cs = (amp * np.cos(w * pos)).astype(np.float32)[:, None]
+        sn = (amp * np.sin(w * pos)).astype(np.float32)[:, None]
+        q[:, :, 2 * c] += cs
+        q[:, :, 2 * c + 1] += sn
+        k[:, :, 2 * c] += cs
+        k[:, :, 2 * c + 1] += sn
+    q[:, :, 32] += np.float32(2.0)
+    for s in range(len(seqlens)):
+        if cu[s + 1] > cu[s]:
+            k[int(cu[s]), :, 32] += np.float32(sink)
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16), cu
