@@ -104,6 +104,21 @@ int tilemix_build_routing(const int32_t* cu_seqlens_h, int32_t batch, int32_t nu
                           int32_t tmpl, int32_t coverage_bp, uint64_t seed, uint64_t* words_h,
                           int32_t* g_h, int64_t* int8_groups_h, int64_t* legal_groups_h);
 
+/* Adaptive routing words (host) -- [Digest, setup]: the evaluated routing is
+ * static, and the interface accepts adaptive policies; [Routes, "Placement
+ * can matter more than the nominal percentage"].  Given the importance of
+ * every legal group (from tilemix_routing_importance, copied to the host),
+ * the legal groups of each (sequence, KV head) are ordered by (importance,
+ * r, G) ascending and the first N8 -- the same count as a template at
+ * coverage_bp -- get bit 1 (INT8).  Words may differ between KV heads.
+ * importance_h: float[num_kv_heads][total_q_tiles][64] (slots of illegal
+ * groups are ignored).  Outputs as tilemix_build_routing.
+ * Errors: EINVAL for bad cu_seqlens or coverage, NULL buffers, or a NaN
+ * importance. */
+int tilemix_build_routing_adaptive(const int32_t* cu_seqlens_h, int32_t batch, int32_t num_kv_heads,
+                                   const float* importance_h, int32_t coverage_bp, uint64_t* words_h,
+                                   int32_t* g_h, int64_t* int8_groups_h, int64_t* legal_groups_h);
+
 /* Work plan (host only) -- the geometry and schedule of one packed batch:
  * per-sequence tile offsets and grouping factors, plus the ordered list of
  * (sequence, query head, query-tile row) work units the fused kernel runs,
@@ -185,6 +200,29 @@ int tilemix_decode_varlen(const int32_t* plan_h, const int32_t* plan_d, const vo
                           const int8_t* k_i8, const int8_t* v_i8, const float* k_scale,
                           const float* v_scale, const uint64_t* words_d, void* workspace,
                           int64_t workspace_bytes, void* out_f16, void* hip_stream);
+
+/* Bytes of device workspace tilemix_routing_importance needs:
+ * (Hq * total_q_tiles + Hkv * total_k_tiles) * d * 4. */
+int tilemix_importance_workspace_size(const int32_t* plan_h, int64_t* bytes);
+
+/* Group importance for adaptive routing (device), a cheap statistic of the
+ * quantiser's output:
+ *   colsum of each int8 block (Q 128-row blocks per query head, K 64-row
+ *   tiles per KV head);
+ *   z(h, r, t) = fl32(dot) * fl32(fl32(s_q * s_k) / (n_q * n_k)), dot the
+ *   exact integer dot product of the Q block's and K tile's colsums, n_q and
+ *   n_k their rows;
+ *   Z(kv, r, t) = max over the KV head's query heads;
+ *   importance(kv, r, G) = max of Z over the group's legal tiles - max of Z
+ *   over the row's legal tiles (binary32), +inf for illegal slots.
+ * Inputs from tilemix_quantize_qk; workspace: device scratch of
+ * tilemix_importance_workspace_size bytes (overwritten); importance_d:
+ * device float[Hkv][total_q_tiles][64].  Sequences of more than 262144
+ * tokens are EUNSUPPORTED. */
+int tilemix_routing_importance(const int32_t* plan_h, const int32_t* plan_d, const int8_t* q_i8,
+                               const int8_t* k_i8, const float* q_scale, const float* k_scale,
+                               void* workspace, int64_t workspace_bytes, float* importance_d,
+                               void* hip_stream);
 
 /* Test hook (device): the int32 accumulator of one 128 x 64 INT8 score tile
  * (sequence seq, query head, query-tile row r, key tile t), computed by the

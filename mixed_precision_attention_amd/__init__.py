@@ -55,6 +55,9 @@ _SIGNATURES = {
     "tilemix_prefill_varlen": ([_P] * 12, ctypes.c_int),
     "tilemix_debug_qk_i32_tile": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
     "tilemix_quantize_kv": ([_P] * 9, ctypes.c_int),
+    "tilemix_build_routing_adaptive": ([_P, _I32, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "tilemix_importance_workspace_size": ([_P, _P], ctypes.c_int),
+    "tilemix_routing_importance": ([_P] * 7 + [_I64, _P, _P], ctypes.c_int),
     "tilemix_decode_workspace_size": ([_P, _P], ctypes.c_int),
     "tilemix_decode_varlen": ([_P] * 9 + [_I64, _P, _P], ctypes.c_int),
 }
@@ -140,6 +143,23 @@ def tilemix_build_routing(cu_seqlens, num_kv_heads: int, template, coverage_bp: 
     return words, g, n8, nl
 
 
+def tilemix_build_routing_adaptive(cu_seqlens, importance, coverage_bp: int):
+    """Words from group importances float32 [Hkv, sum Tm, 64]; returns as
+    tilemix_build_routing."""
+    cu = _host_i32(cu_seqlens)
+    batch = len(cu) - 1
+    imp = np.ascontiguousarray(np.asarray(importance, dtype=np.float32))
+    hkv = imp.shape[0]
+    _, tq, _ = tilemix_query_sizes(cu)
+    words = np.zeros((hkv, tq), dtype=np.uint64)
+    g = np.zeros(batch, dtype=np.int32)
+    n8 = np.zeros(batch, dtype=np.int64)
+    nl = np.zeros(batch, dtype=np.int64)
+    _check(lib().tilemix_build_routing_adaptive(_hptr(cu), batch, hkv, _hptr(imp), int(coverage_bp),
+                                                _hptr(words), _hptr(g), _hptr(n8), _hptr(nl)))
+    return words, g, n8, nl
+
+
 def tilemix_build_plan(cu_seqlens, hq: int, hkv: int, head_dim: int) -> np.ndarray:
     cu = _host_i32(cu_seqlens)
     n = ctypes.c_int64(0)
@@ -177,6 +197,23 @@ def tilemix_debug_qk_i32_tile(plan_h, plan_d, q_i8, k_i8, seq: int, head: int, r
     _check(lib().tilemix_debug_qk_i32_tile(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q_i8, torch.int8, "q_i8"),
         _dptr(k_i8, torch.int8, "k_i8"), seq, head, r, t, _dptr(acc, torch.int32, "acc"),
+        _stream(stream)))
+
+
+def tilemix_importance_workspace_size(plan_h) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().tilemix_importance_workspace_size(_hptr(plan_h), ctypes.byref(n)))
+    return int(n.value)
+
+
+def tilemix_routing_importance(plan_h, plan_d, q_i8, k_i8, q_scale, k_scale, workspace, importance,
+                               stream=None):
+    import torch
+    _check(lib().tilemix_routing_importance(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q_i8, torch.int8, "q_i8"),
+        _dptr(k_i8, torch.int8, "k_i8"), _dptr(q_scale, torch.float32, "q_scale"),
+        _dptr(k_scale, torch.float32, "k_scale"), _dptr(workspace, torch.uint8, "workspace"),
+        workspace.numel() if workspace is not None else 0, _dptr(importance, torch.float32, "importance"),
         _stream(stream)))
 
 
@@ -236,6 +273,24 @@ class TileMixPrefill:
             self.cu, self.hkv, template, coverage_bp, seed)
         w = self.words if self.words.size else np.zeros((1, 1), dtype=np.uint64)
         self.words_d = torch.from_numpy(w.view(np.int64)).to(self.device)
+
+    def set_routing_adaptive(self, coverage_bp: int, stream=None):
+        """Content-dependent words from the quantised Q and K of the last
+        ``quantize`` call (device statistic, host ranking, upload)."""
+        import torch
+        if not hasattr(self, "imp_ws"):
+            self.imp_ws = torch.empty(max(tilemix_importance_workspace_size(self.plan_h), 16),
+                                      dtype=torch.uint8, device=self.device)
+            self.importance = torch.empty((self.hkv, max(self.tq, 1), 64), dtype=torch.float32,
+                                          device=self.device)
+        tilemix_routing_importance(self.plan_h, self.plan_d, self.q_i8, self.k_i8, self.q_scale,
+                                   self.k_scale, self.imp_ws, self.importance, stream)
+        imp = self.importance.cpu().numpy()[:, :self.tq]
+        self.words, self.g, self.n_int8, self.n_legal = tilemix_build_routing_adaptive(
+            self.cu, imp, coverage_bp)
+        w = self.words if self.words.size else np.zeros((1, 1), dtype=np.uint64)
+        self.words_d = torch.from_numpy(w.view(np.int64)).to(self.device)
+        return imp
 
     def quantize(self, q, k, stream=None):
         tilemix_quantize_qk(self.plan_h, self.plan_d, q, k, self.q_i8, self.k_i8, self.q_scale,

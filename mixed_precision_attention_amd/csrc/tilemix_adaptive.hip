@@ -1,0 +1,229 @@
+// Per-group importance for adaptive routing words (gfx950).
+//
+// [Digest, setup]: the evaluated routing is static and data-free, and the
+// interface accepts adaptive policies; [Routes, "Placement can matter more
+// than the nominal percentage"]: where reduced precision lands matters more
+// than how much of it there is.  This is a cheap content statistic built
+// from what the quantiser already produced:
+//   * column sums of each int8 block's codes (Q: 128-row blocks per query
+//     head, K: 64-row tiles per KV head);
+//   * pooled score z(h, r, t) = fl32(dot) * fl32(fl32(s_q * s_k) / (n_q n_k)),
+//     dot the exact integer dot product of the two column-sum vectors, n_q,
+//     n_k the rows of the blocks (mean query against mean key);
+//   * Z(kv, r, t) = max over the KV head's query heads;
+//   * importance of group (r, G) = max of Z over its legal tiles minus the max
+//     of Z over the row's legal tiles (binary32).
+// The host ranks the groups of each (sequence, KV head) by (importance, r, G)
+// and routes the first N8 to INT8 (tilemix_build_routing_adaptive).  All
+// arithmetic is exact or a fixed sequence of IEEE binary32 operations, so the
+// result is reproducible bit for bit.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "tilemix.h"
+#include "tilemix_host.h"
+#include "tilemix_internal.h"
+
+namespace tilemix {
+namespace adaptive {
+
+constexpr int kThreads = 256;
+constexpr int kMaxRowTiles = 4096;  // key tiles of one row held in LDS
+
+struct ImpArgs {
+  const int32_t* plan;
+  const int8_t* qi8;
+  const int8_t* ki8;
+  const float* qs;
+  const float* ks;
+  int32_t* qsum;  // [Hq][tq][D]
+  int32_t* ksum;  // [Hkv][tk][D]
+  float* imp;     // [Hkv][tq][64]
+  int32_t hq, hkv, batch, tq, tk;
+};
+
+__device__ inline int seq_of_tile(const int32_t* seqtab, int batch, int field, int tile) {
+  int lo = 0, hi = batch - 1;  // last sequence whose first tile is <= tile
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seqtab[mid * kSeqStride + field] <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Column sums of one (block, head): thread (4 columns, row part).
+template <int D>
+__global__ __launch_bounds__(kThreads) void block_colsum_kernel(ImpArgs a) {
+  constexpr int kGroups = D / 4, kParts = kThreads / kGroups;
+  __shared__ int part[kParts][D];
+  const int32_t* seqtab = a.plan + kHeaderLen;
+  int bid = blockIdx.x;
+  const bool is_k = bid >= a.tq * a.hq;
+  if (is_k) bid -= a.tq * a.hq;
+  const int H = is_k ? a.hkv : a.hq, blk = is_k ? kBlockN : kBlockM;
+  const int tile = bid / H, head = bid % H;
+  const int s = seq_of_tile(seqtab, a.batch, is_k ? kSeqKtOff : kSeqQtOff, tile);
+  const int32_t* rec = seqtab + s * kSeqStride;
+  const int local = tile - rec[is_k ? kSeqKtOff : kSeqQtOff];
+  const int row0 = rec[kSeqStart] + local * blk;
+  const int nrows = min(blk, rec[kSeqLen] - local * blk);
+  const int8_t* src = (is_k ? a.ki8 : a.qi8) + ((size_t)row0 * H + head) * D;
+  const int tid = threadIdx.x, c4 = tid % kGroups, p = tid / kGroups;
+  int acc[4] = {0, 0, 0, 0};
+  for (int r = p; r < nrows; r += kParts) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (size_t)r * H * D + c4 * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += (int)(int8_t)((w >> (8 * e)) & 0xff);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) part[p][c4 * 4 + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < kParts; ++q) sum += part[q][tid];
+    int32_t* dst = is_k ? a.ksum + ((size_t)head * a.tk + tile) * D : a.qsum + ((size_t)head * a.tq + tile) * D;
+    dst[tid] = sum;
+  }
+}
+
+// Importance of every group of one (KV head, query-tile row).
+template <int D>
+__global__ __launch_bounds__(kThreads) void importance_kernel(ImpArgs a) {
+  __shared__ float zt[kMaxRowTiles];
+  __shared__ float red[kThreads / 64];
+  extern __shared__ int32_t qsum_l[];  // [grp][D]
+  const int32_t* seqtab = a.plan + kHeaderLen;
+  const int kv = blockIdx.x / a.tq, tile = blockIdx.x % a.tq;
+  const int s = seq_of_tile(seqtab, a.batch, kSeqQtOff, tile);
+  const int32_t* rec = seqtab + s * kSeqStride;
+  const int r = tile - rec[kSeqQtOff], L = rec[kSeqLen], g = rec[kSeqG], kt0 = rec[kSeqKtOff];
+  const int nt = min(kBlockM * r + kBlockM - 1, L - 1) / kBlockN + 1;
+  const int grp = a.hq / a.hkv, h0 = kv * grp;
+  const int nq = min(kBlockM, L - kBlockM * r);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < grp * D; i += kThreads)
+    qsum_l[i] = a.qsum[((size_t)(h0 + i / D) * a.tq + tile) * D + i % D];
+  __syncthreads();
+  float rowmax = -INFINITY;
+  for (int t = tid; t < nt; t += kThreads) {
+    const int kt = kt0 + t;
+    const int nk = min(kBlockN, L - kBlockN * t);
+    const int32_t* ksr = a.ksum + ((size_t)kv * a.tk + kt) * D;
+    const float sk = a.ks[(size_t)kv * a.tk + kt];
+    float Z = -INFINITY;
+    for (int h = 0; h < grp; ++h) {
+      long long dot = 0;
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) dot += (long long)qsum_l[h * D + c] * (long long)ksr[c];
+      const float aa = __fmul_rn(a.qs[(size_t)(h0 + h) * a.tq + tile], sk);
+      const float b = __fdiv_rn(aa, (float)(nq * nk));
+      Z = fmaxf(Z, __fmul_rn((float)dot, b));
+    }
+    zt[t] = Z;
+    rowmax = fmaxf(rowmax, Z);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) rowmax = fmaxf(rowmax, __shfl_xor(rowmax, off));
+  if ((tid & 63) == 0) red[tid >> 6] = rowmax;
+  __syncthreads();
+  rowmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int ngroups = (nt - 1) / g + 1;
+  if (tid < kWordBits) {
+    float v = INFINITY;  // illegal groups
+    if (tid < ngroups) {
+      float zg = -INFINITY;
+      for (int t = tid * g; t < min(tid * g + g, nt); ++t) zg = fmaxf(zg, zt[t]);
+      v = __fsub_rn(zg, rowmax);
+    }
+    a.imp[((size_t)kv * a.tq + tile) * kWordBits + tid] = v;
+  }
+}
+
+}  // namespace adaptive
+}  // namespace tilemix
+
+using namespace tilemix;
+using namespace tilemix::adaptive;
+
+namespace {
+
+int check_ptr(const void* p, const char* name, bool needed) {
+  if (!needed) return TILEMIX_OK;
+  if (p == nullptr) return fail(TILEMIX_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(TILEMIX_EINVAL, "%s is not 16-byte aligned", name);
+  return TILEMIX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tilemix_importance_workspace_size(const int32_t* plan_h, int64_t* bytes) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  if (bytes == nullptr) return fail(TILEMIX_EINVAL, "bytes is NULL");
+  *bytes = ((int64_t)plan_h[kHq] * plan_h[kTotalQTiles] + (int64_t)plan_h[kHkv] * plan_h[kTotalKTiles]) *
+           plan_h[kHeadDim] * (int64_t)sizeof(int32_t);
+  return TILEMIX_OK;
+}
+
+int tilemix_routing_importance(const int32_t* plan_h, const int32_t* plan_d, const int8_t* q_i8,
+                               const int8_t* k_i8, const float* q_scale, const float* k_scale,
+                               void* workspace, int64_t workspace_bytes, float* importance_d,
+                               void* hip_stream) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const bool any = plan_h[kTotalTokens] > 0;
+  if ((rc = check_ptr(plan_d, "plan_d", true)) || (rc = check_ptr(q_i8, "q_i8", any)) ||
+      (rc = check_ptr(k_i8, "k_i8", any)) || (rc = check_ptr(q_scale, "q_scale", any)) ||
+      (rc = check_ptr(k_scale, "k_scale", any)) || (rc = check_ptr(workspace, "workspace", any)) ||
+      (rc = check_ptr(importance_d, "importance_d", any)))
+    return rc;
+  int64_t need = 0;
+  tilemix_importance_workspace_size(plan_h, &need);
+  if (workspace_bytes < need)
+    return fail(TILEMIX_EINVAL, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes,
+                (long long)need);
+  for (int32_t s = 0; s < plan_h[kBatch]; ++s)
+    if (plan_h[kHeaderLen + s * kSeqStride + kSeqTn] > kMaxRowTiles)
+      return fail(TILEMIX_EUNSUPPORTED, "sequence %d is longer than %d tokens", s, kMaxRowTiles * kBlockN);
+  if (!any) return TILEMIX_OK;
+  ImpArgs a;
+  a.plan = plan_d;
+  a.qi8 = q_i8;
+  a.ki8 = k_i8;
+  a.qs = q_scale;
+  a.ks = k_scale;
+  a.hq = plan_h[kHq];
+  a.hkv = plan_h[kHkv];
+  a.batch = plan_h[kBatch];
+  a.tq = plan_h[kTotalQTiles];
+  a.tk = plan_h[kTotalKTiles];
+  a.qsum = static_cast<int32_t*>(workspace);
+  a.ksum = a.qsum + (size_t)a.hq * a.tq * plan_h[kHeadDim];
+  a.imp = importance_d;
+  const int d = plan_h[kHeadDim];
+  const int64_t b1 = (int64_t)a.tq * a.hq + (int64_t)a.tk * a.hkv, b2 = (int64_t)a.hkv * a.tq;
+  if (b1 > 0x7fffffff || b2 > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  const size_t lds = (size_t)(a.hq / a.hkv) * d * sizeof(int32_t);
+  if (lds > 64 * 1024) return fail(TILEMIX_EUNSUPPORTED, "too many query heads per KV head");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (d == 64) {
+    hipLaunchKernelGGL(block_colsum_kernel<64>, dim3((unsigned)b1), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(importance_kernel<64>, dim3((unsigned)b2), dim3(kThreads), lds, st, a);
+  } else {
+    hipLaunchKernelGGL(block_colsum_kernel<128>, dim3((unsigned)b1), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(importance_kernel<128>, dim3((unsigned)b2), dim3(kThreads), lds, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TILEMIX_EHIP, "importance launch: %s", hipGetErrorString(e));
+  return TILEMIX_OK;
+}
+
+}  // extern "C"

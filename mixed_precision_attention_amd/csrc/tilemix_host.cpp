@@ -388,6 +388,56 @@ int tilemix_build_routing(const int32_t* cu_seqlens_h, int32_t batch, int32_t nu
   return TILEMIX_OK;
 }
 
+int tilemix_build_routing_adaptive(const int32_t* cu_seqlens_h, int32_t batch, int32_t num_kv_heads,
+                                   const float* importance_h, int32_t coverage_bp, uint64_t* words_h,
+                                   int32_t* g_h, int64_t* int8_groups_h, int64_t* legal_groups_h) {
+  clear_error();
+  int rc = check_cu_seqlens(cu_seqlens_h, batch);
+  if (rc) return rc;
+  if (num_kv_heads <= 0) return fail(TILEMIX_EINVAL, "num_kv_heads must be > 0");
+  if (coverage_bp < 0 || coverage_bp > 10000)
+    return fail(TILEMIX_EINVAL, "coverage_bp must be in [0, 10000] (got %d)", coverage_bp);
+  int64_t total_tm = 0;
+  for (int32_t s = 0; s < batch; ++s) total_tm += geometry(cu_seqlens_h[s + 1] - cu_seqlens_h[s]).Tm;
+  if (total_tm > 0 && (words_h == nullptr || importance_h == nullptr))
+    return fail(TILEMIX_EINVAL, "words_h and importance_h must not be NULL");
+  try {
+    int64_t off = 0;
+    std::vector<Group> groups;
+    for (int32_t s = 0; s < batch; ++s) {
+      const SeqGeo geo = geometry(cu_seqlens_h[s + 1] - cu_seqlens_h[s]);
+      groups.clear();
+      for (int64_t r = 0; r < geo.Tm; ++r)
+        for (int64_t G = 0; G <= geo.last_group(r); ++G) groups.push_back({(int32_t)r, (int32_t)G});
+      const int64_t n_legal = (int64_t)groups.size();
+      const int64_t n8 = (coverage_bp * n_legal + 5000) / 10000;
+      for (int32_t h = 0; h < num_kv_heads; ++h) {
+        const float* imp = importance_h + ((int64_t)h * total_tm + off) * TILEMIX_WORD_BITS;
+        auto key = [&](const Group& x) { return imp[(int64_t)x.r * TILEMIX_WORD_BITS + x.G]; };
+        for (const Group& x : groups)
+          if (key(x) != key(x)) return fail(TILEMIX_EINVAL, "importance of sequence %d is NaN", s);
+        // least important first; ties by (r, G)
+        std::vector<Group> order = groups;
+        std::stable_sort(order.begin(), order.end(), [&](const Group& a, const Group& b) {
+          const float ka = key(a), kb = key(b);
+          if (ka != kb) return ka < kb;
+          return a.r != b.r ? a.r < b.r : a.G < b.G;
+        });
+        uint64_t* w = words_h + (int64_t)h * total_tm + off;
+        std::memset(w, 0, geo.Tm * sizeof(uint64_t));
+        for (int64_t i = 0; i < n8; ++i) w[order[i].r] |= 1ull << order[i].G;
+      }
+      off += geo.Tm;
+      if (g_h) g_h[s] = (int32_t)geo.g;
+      if (int8_groups_h) int8_groups_h[s] = n8;
+      if (legal_groups_h) legal_groups_h[s] = n_legal;
+    }
+  } catch (const std::exception& e) {
+    return fail(TILEMIX_EINVAL, "adaptive routing build failed: %s", e.what());
+  }
+  return TILEMIX_OK;
+}
+
 int tilemix_plan_size(const int32_t* cu_seqlens_h, int32_t batch, int32_t hq, int32_t hkv,
                       int32_t head_dim, int64_t* plan_len) {
   clear_error();

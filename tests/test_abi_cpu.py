@@ -142,6 +142,45 @@ def test_errors_are_reported():
                                    None) == -2
 
 
+@pytest.mark.parametrize("lens,hkv", [([256], 1), ([1024, 300, 1, 0, 129], 3), ([4160, 8192], 2)])
+def test_adaptive_routing_bit_exact_with_oracle(lens, hkv):
+    geos = [oracle.seq_geometry(L) for L in lens]
+    rng = np.random.default_rng(len(lens))
+    tm_total = sum(g.Tm for g in geos)
+    imp = np.full((hkv, tm_total, 64), np.inf, dtype=np.float32)
+    off = 0
+    for geo in geos:
+        for r in range(geo.Tm):
+            # few distinct values, so ties (broken by (r, G)) are common
+            imp[:, off + r, :geo.D[r] + 1] = -rng.integers(0, 4, size=(hkv, geo.D[r] + 1)) * np.float32(0.5)
+        off += geo.Tm
+    cu = synth.cu_seqlens_of(lens)
+    for cov in (0, 1000, 2500, 5000, 7500, 10000):
+        w, g, n8, nl = tm.tilemix_build_routing_adaptive(cu, imp, cov)
+        ow, og, on8, onl = oracle.adaptive_words(lens, imp, cov)
+        assert np.array_equal(w, ow), cov
+        assert np.array_equal(g, og) and np.array_equal(n8, on8) and np.array_equal(nl, onl)
+    bad = imp.copy()
+    bad[0, 0, 0] = np.nan
+    with pytest.raises(tm.TileMixError, match="NaN"):
+        tm.tilemix_build_routing_adaptive(cu, bad, 5000)
+
+
+def test_importance_host_checks():
+    cu = synth.cu_seqlens_of([300, 0, 4096])
+    plan = tm.tilemix_build_plan(cu, 6, 2, 128)
+    _, tq, tk = tm.tilemix_query_sizes(cu)
+    assert tm.tilemix_importance_workspace_size(plan) == (6 * tq + 2 * tk) * 128 * 4
+    lib = tm.lib()
+    p = ctypes.c_void_p(plan.ctypes.data)
+    fake = ctypes.c_void_p(16)
+    assert lib.tilemix_routing_importance(p, fake, fake, fake, fake, fake, fake, 100, fake, None) == -1
+    assert "workspace" in tm.tilemix_last_error()
+    long_plan = tm.tilemix_build_plan(synth.cu_seqlens_of([262145]), 1, 1, 64)
+    assert lib.tilemix_routing_importance(ctypes.c_void_p(long_plan.ctypes.data), fake, fake, fake, fake,
+                                          fake, fake, 1 << 40, fake, None) == -2
+
+
 def test_decode_host_checks():
     cu = synth.cu_seqlens_of([300, 0, 4096])
     plan = tm.tilemix_build_plan(cu, 6, 2, 128)
