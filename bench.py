@@ -15,6 +15,10 @@ fp16-equivalent TFLOP/s (INT8 operations weighted by the fp16/int8 peak
 ratio) against the published MI355X dense fp16 MFMA peak, i.e. ``frac`` is
 the coverage-weighted MFMA roofline time over the measured kernel time.
 
+``adaptive`` (skip with --no-adaptive) times the content-dependent routing
+statistic, the host ranking, and the prefill under the resulting words at the
+same coverage.
+
 ``decode`` (skip with --no-decode) times one decode step per sequence against
 an INT8 key/value cache holding the same workload's K and V: tokens/s is new
 tokens per second, and its roofline is HBM bandwidth over the step's
@@ -42,9 +46,11 @@ KERNEL_SRC = os.path.join(ROOT, "mixed_precision_attention_amd", "csrc", "tilemi
 
 def legal_pair_counts(cu, words, hq, hkv):
     """(P, P8): legal causal (query, key) pairs over all query heads, and the
-    ones lying in INT8-routed groups -- counted exactly from the words."""
+    ones lying in INT8-routed groups -- counted exactly from each KV head's
+    words (query head h uses the words of KV head h // (Hq/Hkv))."""
     import numpy as np
-    P = P8 = 0
+    P = 0
+    P8 = [0] * hkv
     row_off = 0
     for s in range(len(cu) - 1):
         L = int(cu[s + 1] - cu[s])
@@ -56,12 +62,13 @@ def legal_pair_counts(cu, words, hq, hkv):
             t = np.arange(last_t + 1)
             # keys of tile t visible to query q: clip(q - 64 t + 1, 0, 64)
             cnt = np.clip(q[:, None] - 64 * t[None, :] + 1, 0, 64).sum(axis=0)
-            w = np.uint64(words[0, row_off + r])
-            bits = ((w >> (t // g).astype(np.uint64)) & np.uint64(1)).astype(np.int64)
             P += int(cnt.sum())
-            P8 += int((cnt * bits).sum())
+            for kv in range(hkv):
+                w = np.uint64(words[kv, row_off + r])
+                bits = ((w >> (t // g).astype(np.uint64)) & np.uint64(1)).astype(np.int64)
+                P8[kv] += int((cnt * bits).sum())
         row_off += Tm
-    return P * hq, P8 * hq
+    return P * hq, sum(P8) * (hq // hkv)
 
 
 def traffic_record(path):
@@ -117,6 +124,53 @@ def write_traffic(args):
         f.write("\n")
     print(json.dumps(rec))
     return 0
+
+
+def bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, steps):
+    """Adaptive routing at the same coverage: the device importance statistic
+    (timed with events), the host ranking and word upload (wall clock), and
+    the prefill under the adaptive words."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    tp.quantize(qd, kd)
+    tp.set_routing_adaptive(coverage)          # warm-up and buffers
+    torch.cuda.synchronize()
+    import mixed_precision_attention_amd as tm
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        tm.tilemix_routing_importance(tp.plan_h, tp.plan_d, tp.q_i8, tp.k_i8, tp.q_scale, tp.k_scale,
+                                      tp.imp_ws, tp.importance)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    imp_us = e0.elapsed_time(e1) * 1e3 / steps
+    t0 = time.perf_counter()
+    tp.set_routing_adaptive(coverage)
+    torch.cuda.synchronize()
+    route_ms = (time.perf_counter() - t0) * 1e3
+    out = torch.empty_like(qd)
+    for _ in range(3):
+        tp.attend(qd, kd, vd, out)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        tp.attend(qd, kd, vd, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = e0.elapsed_time(e1) / steps
+    P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
+    t_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    tq, tk = sum(-(-int(L) // 128) for L in lens), sum(-(-int(L) // 64) for L in lens)
+    imp_bytes = int(lens.sum()) * (hq + hkv) * d + (hq * tq + hkv * tk) * d * 4 * 2 + hkv * tq * 64 * 4
+    return {"coverage_bp": coverage, "importance_us": imp_us,
+            "importance_roofline": {"bound": "hbm", "achieved": imp_bytes / (imp_us * 1e-6) / 1e9,
+                                    "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                    "frac": imp_bytes / (imp_us * 1e-6) / PEAK_HBM,
+                                    "algorithmic_bytes": imp_bytes},
+            "route_total_ms": route_ms, "prefill_ms": attn_ms, "frac": t_roof / (attn_ms * 1e-3),
+            "int8_pair_share": P8 / P}
 
 
 def decode_bytes(cu, hq, hkv, d, tq, tk):
@@ -278,6 +332,8 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode step over the INT8 key/value cache")
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-adaptive", action="store_true",
+                    help="skip the adaptive-routing leg (importance statistic + prefill under its words)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
@@ -398,6 +454,8 @@ def main(argv=None):
                       "roofline_us": t_roof * 1e6, "host_build_ms": host_build_ms,
                       "wall_s": wall},
     }
+    if not args.no_adaptive:
+        result["adaptive"] = bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, 20)
     if not args.no_decode:
         spec_named = dict(spec, name=args.workload)
         result["decode"] = bench_decode(q, k, v, cu, spec_named, template, coverage, args.decode_steps,
