@@ -7,4 +7,6 @@ from .tilemix_oracle import (BLOCK_M, BLOCK_N, TEMPLATES, SeqGeometry, seq_geome
                              splitmix64_mix, rowrandom_hash, sptrans_stride, union_orders,
                              softmax_scale, int8_tile_scale, quantize_kv_cache,
                              quantize_query_rows, decode_attention, block_column_sums,
-                             routing_importance, adaptive_words, importance_exposure)
+                             routing_importance, adaptive_words, importance_exposure, FP8_MAX,
+                             fp8_e4m3_decode, fp8_e4m3_encode, quantize_blocks_fp8, routing_words3,
+                             prefill_attention3)

@@ -692,3 +692,169 @@ def importance_exposure(q, k, cu_seqlens, hq: int, hkv: int, words, tau: float =
                 inside += float(p[sel][bits == 1].sum())
                 total += float(p[sel].sum())
     return inside / total if total else 0.0
+
+
+# ---------------------------------------------------------------------------
+# A third precision: FP8 (E4M3) score tiles
+# ---------------------------------------------------------------------------
+#
+# [Digest, setup] / [Explainer, 写在后面]: the authors note that moving to
+# FP8 or INT4 needs the scales and the schedule redone; the pages leave it
+# open.  Readings taken here:
+#   * FP8 is the OCP E4M3 format (1 sign, 4 exponent bits with bias 7, 3
+#     mantissa bits, subnormals, largest finite 448, no infinities);
+#   * Q and K are quantised in the same blocks as INT8 (128 x d, 64 x d),
+#     s = fl32(absmax / 448), code = E4M3 round-half-even of fl32(x / s), an
+#     all-zero block has s = 0 and codes 0;
+#   * an FP8 tile's score is S = (sum of q8 * k8 over d) * fl32(fl32(s_q s_k)
+#     * fl32(1/sqrt(d))) -- exact products, one score domain with the others;
+#   * routing has three classes: a template's order keeps its first groups
+#     in FP16, the next ones in FP8 and the last ones in INT8; with INT8
+#     coverage c8 and FP8 coverage cf, N8 = round(c8 N_legal) and
+#     N8 + Nf8 = round((c8 + cf) N_legal), so the FP8-or-INT8 set is the
+#     INT8 set of coverage c8 + cf.  A second word per (KV head, row) marks the
+#     FP8 groups.
+
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes):
+    """Values of E4M3 codes (uint8 array) as float64; 0x7F/0xFF are NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+    return sign * val
+
+
+def fp8_e4m3_encode(x):
+    """Round-half-even of binary32 values onto the E4M3 grid (|x| <= 464
+    stays finite; larger magnitudes are saturated to 448)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    # exponent of the binade (subnormal range uses the spacing of 2^-6)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    e = np.minimum(e, 8.0)
+    step = np.exp2(e - 3.0)
+    q = np.round(a / step)             # numpy rounds half to even
+    mag = q * step
+    mag = np.minimum(mag, FP8_MAX)
+    # encode magnitude
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = mag < 2.0 ** -6
+    code = np.where(sub, np.round(mag / 2.0 ** -9).astype(np.int64), code)
+    en = np.floor(np.log2(np.where(sub, 1.0, mag)))
+    mant = np.round((np.where(sub, 1.0, mag) / np.exp2(en) - 1.0) * 8.0).astype(np.int64)
+    code = np.where(sub, code, ((en.astype(np.int64) + 7) << 3) | mant)
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_blocks_fp8(x: np.ndarray, cu_seqlens, block: int):
+    """Blockwise FP8 (E4M3) quantisation: s = fl32(absmax / 448), codes
+    E4M3(fl32(x / s)).  Returns (uint8 [T, H, d], float32 [H, tiles])."""
+    cu = [int(c) for c in cu_seqlens]
+    T, H, d = x.shape
+    q = np.zeros((T, H, d), dtype=np.uint8)
+    scales = []
+    for s in range(len(cu) - 1):
+        start, end = cu[s], cu[s + 1]
+        for b0 in range(start, end, block):
+            b1 = min(b0 + block, end)
+            blk = x[b0:b1].astype(np.float32)
+            a = np.abs(blk).max(axis=(0, 2))
+            sc = (a / np.float32(FP8_MAX)).astype(np.float32)
+            qb = np.zeros(blk.shape, dtype=np.uint8)
+            for h in range(H):
+                if a[h] == 0:
+                    continue
+                qb[:, h, :] = fp8_e4m3_encode((blk[:, h, :] / sc[h]).astype(np.float32))
+            q[b0:b1] = qb
+            scales.append(sc)
+    sc_all = np.stack(scales, axis=1).astype(np.float32) if scales else np.zeros((H, 0), dtype=np.float32)
+    return q, sc_all
+
+
+def routing_words3(seqlens, num_kv_heads: int, template: str, int8_bp: int, fp8_bp: int, seed: int = 0):
+    """Three-class routing: (INT8 words, FP8 words, g, N8, Nf8, N_legal)."""
+    if int8_bp + fp8_bp > 10000:
+        raise ValueError("INT8 + FP8 coverage above 100%")
+    geos = [seq_geometry(int(L)) for L in seqlens]
+    total_tm = sum(geo.Tm for geo in geos)
+    w8 = np.zeros((num_kv_heads, total_tm), dtype=np.uint64)
+    wf = np.zeros((num_kv_heads, total_tm), dtype=np.uint64)
+    gs, n8s, nfs, nls = [], [], [], []
+    off = 0
+    for geo in geos:
+        order = template_order(geo, template, seed)
+        n = len(order)
+        n8 = int8_group_count(int8_bp, n)
+        nboth = int8_group_count(int8_bp + fp8_bp, n)
+        for (r, G) in order[n - n8:]:
+            w8[:, off + r] |= np.uint64(1 << G)
+        for (r, G) in order[n - nboth:n - n8]:
+            wf[:, off + r] |= np.uint64(1 << G)
+        gs.append(geo.g)
+        n8s.append(n8)
+        nfs.append(nboth - n8)
+        nls.append(n)
+        off += geo.Tm
+    return (w8, wf, np.array(gs, dtype=np.int32), np.array(n8s, dtype=np.int64),
+            np.array(nfs, dtype=np.int64), np.array(nls, dtype=np.int64))
+
+
+def prefill_attention3(q, k, v, q_i8, k_i8, q_scale, k_scale, q_f8, k_f8, q_scale_f8, k_scale_f8,
+                       words_i8, words_f8, cu_seqlens, hq: int, hkv: int, rows=None, round_p: bool = True):
+    """Causal varlen prefill with three score paths per group: INT8 (bit of
+    ``words_i8``), FP8 (bit of ``words_f8``) or FP16.  Same steps as
+    ``prefill_attention``; an FP8 tile's score is the exact dot product of
+    the decoded E4M3 codes times fl32(fl32(s_q s_k) * fl32(1/sqrt(d)))."""
+    cu = [int(c) for c in cu_seqlens]
+    seqlens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    T, _, d = q.shape
+    grp = hq // hkv
+    qt_off, kt_off = _tile_offsets(seqlens)
+    inv_sqrt_d = softmax_scale(d)
+    out = np.zeros((T, hq, d), dtype=np.float64)
+    if rows is None:
+        rows = [(s, h, r) for s in range(len(seqlens)) for h in range(hq)
+                for r in range(seq_geometry(seqlens[s]).Tm)]
+    qf8v = fp8_e4m3_decode(q_f8)
+    kf8v = fp8_e4m3_decode(k_f8)
+    for (s, h, r) in rows:
+        L = seqlens[s]
+        geo = seq_geometry(L)
+        start = cu[s]
+        kv = h // grp
+        w8 = int(words_i8[kv, qt_off[s] + r])
+        wf = int(words_f8[kv, qt_off[s] + r])
+        q0, q1 = BLOCK_M * r, min(BLOCK_M * r + BLOCK_M, L)
+        nk = min(geo.last_tile[r] * BLOCK_N + BLOCK_N, L)
+        S = np.empty((q1 - q0, nk), dtype=np.float64)
+        qf = q[start + q0:start + q1, h, :].astype(np.float64)
+        qi = q_i8[start + q0:start + q1, h, :].astype(np.float64)
+        q8 = qf8v[start + q0:start + q1, h, :]
+        for t in range(geo.last_tile[r] + 1):
+            G = t // geo.g
+            k0, k1 = BLOCK_N * t, min(BLOCK_N * t + BLOCK_N, L)
+            if (w8 >> G) & 1:
+                acc = qi @ k_i8[start + k0:start + k1, kv, :].astype(np.float64).T
+                S[:, k0:k1] = acc * np.float64(int8_tile_scale(q_scale[h, qt_off[s] + r],
+                                                               k_scale[kv, kt_off[s] + t], d))
+            elif (wf >> G) & 1:
+                acc = q8 @ kf8v[start + k0:start + k1, kv, :].T
+                S[:, k0:k1] = acc * np.float64(int8_tile_scale(q_scale_f8[h, qt_off[s] + r],
+                                                               k_scale_f8[kv, kt_off[s] + t], d))
+            else:
+                kf = k[start + k0:start + k1, kv, :].astype(np.float64)
+                S[:, k0:k1] = (qf @ kf.T) * np.float64(inv_sqrt_d)
+        qpos = np.arange(q0, q1)[:, None]
+        S = np.where(np.arange(nk)[None, :] <= qpos, S, -np.inf)
+        p = np.exp(S - S.max(axis=1, keepdims=True))
+        if round_p:
+            p = p.astype(np.float16).astype(np.float64)
+        vf = v[start:start + nk, kv, :].astype(np.float64)
+        out[start + q0:start + q1, h, :] = (p @ vf) / p.sum(axis=1, keepdims=True)
+    return out

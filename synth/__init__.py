@@ -152,3 +152,23 @@ def make_qkv_local(seqlens, hq: int, hkv: int, d: int, seed: int = 0, amp: float
         if cu[s + 1] > cu[s]:
             k[int(cu[s]), :, 32] += np.float32(sink)
     return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16), cu
+
+
+def lossless_blocks_fp8(seqlens, heads: int, d: int, block: int, seed: int = 0):
+    """Values that blockwise E4M3 quantisation reproduces exactly: every
+    (block, head) holds E4M3 grid values (|v| >= 1) times 2^-e, e in
+    [4, 9], with one entry of +-448 * 2^-e, so the scale is exactly 2^-e."""
+    grid = np.array([(1.0 + m / 8.0) * 2.0 ** x for x in range(0, 9) for m in range(8)
+                     if (1.0 + m / 8.0) * 2.0 ** x <= 448.0])
+    cu = cu_seqlens_of(seqlens)
+    rng = np.random.default_rng(seed)
+    t = int(cu[-1])
+    vals = grid[rng.integers(0, len(grid), size=(t, heads, d))] * np.where(rng.random((t, heads, d)) < 0.5, -1, 1)
+    for s in range(len(seqlens)):
+        start, end = int(cu[s]), int(cu[s + 1])
+        for b0 in range(start, end, block):
+            b1 = min(b0 + block, end)
+            vals[b0, :, 0] = 448.0 * np.where(rng.random(heads) < 0.5, -1, 1)
+            e = rng.integers(4, 10, size=heads).astype(np.float64)
+            vals[b0:b1] *= np.exp2(-e)[None, :, None]
+    return vals.astype(np.float16)
