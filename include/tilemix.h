@@ -104,6 +104,20 @@ int tilemix_build_routing(const int32_t* cu_seqlens_h, int32_t batch, int32_t nu
                           int32_t tmpl, int32_t coverage_bp, uint64_t seed, uint64_t* words_h,
                           int32_t* g_h, int64_t* int8_groups_h, int64_t* legal_groups_h);
 
+/* Three-class routing (host) -- a third precision, FP8 (OCP E4M3), for the
+ * open question of [Digest, setup] / [Explainer, 写在后面] (moving to FP8
+ * needs scales and schedule redone).  The template's order keeps its first
+ * groups FP16, the next FP8, the last INT8: N8 = floor((int8_bp * N_legal +
+ * 5000) / 10000) and N8 + Nf8 = the same with int8_bp + fp8_bp, so the INT8
+ * word equals tilemix_build_routing's at int8_bp and INT8 | FP8 equals it at
+ * int8_bp + fp8_bp.  words_f8_h marks FP8 groups (disjoint from INT8).
+ * Errors: EINVAL when int8_bp + fp8_bp > 10000, else as
+ * tilemix_build_routing. */
+int tilemix_build_routing3(const int32_t* cu_seqlens_h, int32_t batch, int32_t num_kv_heads, int32_t tmpl,
+                           int32_t int8_bp, int32_t fp8_bp, uint64_t seed, uint64_t* words_i8_h,
+                           uint64_t* words_f8_h, int32_t* g_h, int64_t* int8_groups_h, int64_t* fp8_groups_h,
+                           int64_t* legal_groups_h);
+
 /* Adaptive routing words (host) -- [Digest, setup]: the evaluated routing is
  * static, and the interface accepts adaptive policies; [Routes, "Placement
  * can matter more than the nominal percentage"].  Given the importance of
@@ -175,6 +189,26 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
 int tilemix_quantize_kv(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16,
                         const void* v_f16, int8_t* k_i8, int8_t* v_i8, float* k_scale,
                         float* v_scale, void* hip_stream);
+
+/* FP8 (E4M3) blockwise quantiser (device): the blocks of tilemix_quantize_qk,
+ * s = fl32(absmax / 448), code = E4M3 round-half-even of fl32(x / s) (IEEE
+ * division); a = 0 gives s = 0 and codes 0.
+ * Outputs: q_f8 [T, Hq, d], k_f8 [T, Hkv, d] (device bytes), q_scale_f8
+ * float[Hq][total_q_tiles], k_scale_f8 float[Hkv][total_k_tiles]. */
+int tilemix_quantize_qk_fp8(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                            const void* k_f16, uint8_t* q_f8, uint8_t* k_f8, float* q_scale_f8,
+                            float* k_scale_f8, void* hip_stream);
+
+/* Three-path fused prefill (device): as tilemix_prefill_varlen, and a group
+ * whose bit is set in words_f8_d (and not in words_i8_d) computes
+ * S = (sum over d of q_f8 * k_f8, E4M3 products, fp32 accumulation) *
+ * (s_q8 * s_k8 / sqrt(d)) on the FP8 matrix cores. */
+int tilemix_prefill_varlen3(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                            const void* k_f16, const void* v_f16, const int8_t* q_i8, const int8_t* k_i8,
+                            const float* q_scale, const float* k_scale, const uint8_t* q_f8,
+                            const uint8_t* k_f8, const float* q_scale_f8, const float* k_scale_f8,
+                            const uint64_t* words_i8_d, const uint64_t* words_f8_d, void* out_f16,
+                            void* hip_stream);
 
 /* Bytes of device workspace tilemix_decode_varlen needs for this plan:
  * B * Hq * ceil(max L / 256) * (d + 2) * 4. */

@@ -55,6 +55,9 @@ _SIGNATURES = {
     "tilemix_prefill_varlen": ([_P] * 12, ctypes.c_int),
     "tilemix_debug_qk_i32_tile": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
     "tilemix_quantize_kv": ([_P] * 9, ctypes.c_int),
+    "tilemix_build_routing3": ([_P, _I32, _I32, _I32, _I32, _I32, _U64, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "tilemix_quantize_qk_fp8": ([_P] * 9, ctypes.c_int),
+    "tilemix_prefill_varlen3": ([_P] * 17, ctypes.c_int),
     "tilemix_build_routing_adaptive": ([_P, _I32, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
     "tilemix_importance_workspace_size": ([_P, _P], ctypes.c_int),
     "tilemix_routing_importance": ([_P] * 7 + [_I64, _P, _P], ctypes.c_int),
@@ -143,6 +146,24 @@ def tilemix_build_routing(cu_seqlens, num_kv_heads: int, template, coverage_bp: 
     return words, g, n8, nl
 
 
+def tilemix_build_routing3(cu_seqlens, num_kv_heads: int, template, int8_bp: int, fp8_bp: int, seed: int = 0):
+    """Returns (INT8 words, FP8 words, g, N8, Nf8, N_legal)."""
+    cu = _host_i32(cu_seqlens)
+    batch = len(cu) - 1
+    tmpl = TEMPLATE_IDS[template] if isinstance(template, str) else int(template)
+    _, tq, _ = tilemix_query_sizes(cu)
+    w8 = np.zeros((max(num_kv_heads, 0), tq), dtype=np.uint64)
+    wf = np.zeros_like(w8)
+    g = np.zeros(batch, dtype=np.int32)
+    n8 = np.zeros(batch, dtype=np.int64)
+    nf = np.zeros(batch, dtype=np.int64)
+    nl = np.zeros(batch, dtype=np.int64)
+    _check(lib().tilemix_build_routing3(_hptr(cu), batch, int(num_kv_heads), tmpl, int(int8_bp), int(fp8_bp),
+                                        ctypes.c_uint64(seed & (2 ** 64 - 1)), _hptr(w8), _hptr(wf), _hptr(g),
+                                        _hptr(n8), _hptr(nf), _hptr(nl)))
+    return w8, wf, g, n8, nf, nl
+
+
 def tilemix_build_routing_adaptive(cu_seqlens, importance, coverage_bp: int):
     """Words from group importances float32 [Hkv, sum Tm, 64]; returns as
     tilemix_build_routing."""
@@ -189,6 +210,28 @@ def tilemix_prefill_varlen(plan_h, plan_d, q, k, v, q_i8, k_i8, q_scale, k_scale
         _dptr(k_i8, torch.int8, "k_i8"), _dptr(q_scale, torch.float32, "q_scale"),
         _dptr(k_scale, torch.float32, "k_scale"), _dptr(words_d, torch.int64, "words_d"),
         _dptr(out, torch.float16, "out"), _stream(stream)))
+
+
+def tilemix_quantize_qk_fp8(plan_h, plan_d, q, k, q_f8, k_f8, q_scale_f8, k_scale_f8, stream=None):
+    import torch
+    _check(lib().tilemix_quantize_qk_fp8(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
+        _dptr(k, torch.float16, "k"), _dptr(q_f8, torch.uint8, "q_f8"), _dptr(k_f8, torch.uint8, "k_f8"),
+        _dptr(q_scale_f8, torch.float32, "q_scale_f8"), _dptr(k_scale_f8, torch.float32, "k_scale_f8"),
+        _stream(stream)))
+
+
+def tilemix_prefill_varlen3(plan_h, plan_d, q, k, v, q_i8, k_i8, q_scale, k_scale, q_f8, k_f8, q_scale_f8,
+                            k_scale_f8, words_i8_d, words_f8_d, out, stream=None):
+    import torch
+    _check(lib().tilemix_prefill_varlen3(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
+        _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(q_i8, torch.int8, "q_i8"),
+        _dptr(k_i8, torch.int8, "k_i8"), _dptr(q_scale, torch.float32, "q_scale"),
+        _dptr(k_scale, torch.float32, "k_scale"), _dptr(q_f8, torch.uint8, "q_f8"),
+        _dptr(k_f8, torch.uint8, "k_f8"), _dptr(q_scale_f8, torch.float32, "q_scale_f8"),
+        _dptr(k_scale_f8, torch.float32, "k_scale_f8"), _dptr(words_i8_d, torch.int64, "words_i8_d"),
+        _dptr(words_f8_d, torch.int64, "words_f8_d"), _dptr(out, torch.float16, "out"), _stream(stream)))
 
 
 def tilemix_debug_qk_i32_tile(plan_h, plan_d, q_i8, k_i8, seq: int, head: int, r: int, t: int,
@@ -307,6 +350,40 @@ class TileMixPrefill:
         self.quantize(q, k, stream)
         self.attend(q, k, v, out, stream)
         return out
+
+
+class TileMixPrefill3(TileMixPrefill):
+    """Three score paths per group -- FP16, FP8 (E4M3) and INT8 -- from a
+    template at INT8 coverage ``int8_bp`` and FP8 coverage ``fp8_bp``."""
+
+    def __init__(self, cu_seqlens, hq: int, hkv: int, head_dim: int, template, int8_bp: int, fp8_bp: int,
+                 seed: int = 0, device="cuda"):
+        import torch
+        super().__init__(cu_seqlens, hq, hkv, head_dim, template, int8_bp, seed, device)
+        self.set_routing3(template, int8_bp, fp8_bp, seed)
+        t = max(self.tokens, 1)
+        self.q_f8 = torch.empty((t, hq, head_dim), dtype=torch.uint8, device=device)
+        self.k_f8 = torch.empty((t, hkv, head_dim), dtype=torch.uint8, device=device)
+        self.q_scale_f8 = torch.empty((hq, max(self.tq, 1)), dtype=torch.float32, device=device)
+        self.k_scale_f8 = torch.empty((hkv, max(self.tk, 1)), dtype=torch.float32, device=device)
+
+    def set_routing3(self, template, int8_bp: int, fp8_bp: int, seed: int = 0):
+        import torch
+        self.words, self.words_f8, self.g, self.n_int8, self.n_fp8, self.n_legal = tilemix_build_routing3(
+            self.cu, self.hkv, template, int8_bp, fp8_bp, seed)
+        for name, w in (("words_d", self.words), ("words_f8_d", self.words_f8)):
+            w = w if w.size else np.zeros((1, 1), dtype=np.uint64)
+            setattr(self, name, torch.from_numpy(w.view(np.int64)).to(self.device))
+
+    def quantize(self, q, k, stream=None):
+        super().quantize(q, k, stream)
+        tilemix_quantize_qk_fp8(self.plan_h, self.plan_d, q, k, self.q_f8, self.k_f8, self.q_scale_f8,
+                                self.k_scale_f8, stream)
+
+    def attend(self, q, k, v, out, stream=None):
+        tilemix_prefill_varlen3(self.plan_h, self.plan_d, q, k, v, self.q_i8, self.k_i8, self.q_scale,
+                                self.k_scale, self.q_f8, self.k_f8, self.q_scale_f8, self.k_scale_f8,
+                                self.words_d, self.words_f8_d, out, stream)
 
 
 class TileMixDecode:

@@ -388,6 +388,50 @@ int tilemix_build_routing(const int32_t* cu_seqlens_h, int32_t batch, int32_t nu
   return TILEMIX_OK;
 }
 
+int tilemix_build_routing3(const int32_t* cu_seqlens_h, int32_t batch, int32_t num_kv_heads, int32_t tmpl,
+                           int32_t int8_bp, int32_t fp8_bp, uint64_t seed, uint64_t* words_i8_h,
+                           uint64_t* words_f8_h, int32_t* g_h, int64_t* int8_groups_h, int64_t* fp8_groups_h,
+                           int64_t* legal_groups_h) {
+  clear_error();
+  int rc = check_cu_seqlens(cu_seqlens_h, batch);
+  if (rc) return rc;
+  if (num_kv_heads <= 0) return fail(TILEMIX_EINVAL, "num_kv_heads must be > 0");
+  if (tmpl < TILEMIX_BAND || tmpl > TILEMIX_SPTRANS)
+    return fail(TILEMIX_EINVAL, "unknown template id %d", tmpl);
+  if (int8_bp < 0 || fp8_bp < 0 || int8_bp + fp8_bp > 10000)
+    return fail(TILEMIX_EINVAL, "coverages must be >= 0 with int8_bp + fp8_bp <= 10000 (got %d, %d)", int8_bp,
+                fp8_bp);
+  int64_t total_tm = 0;
+  for (int32_t s = 0; s < batch; ++s) total_tm += geometry(cu_seqlens_h[s + 1] - cu_seqlens_h[s]).Tm;
+  if (total_tm > 0 && (words_i8_h == nullptr || words_f8_h == nullptr))
+    return fail(TILEMIX_EINVAL, "words_i8_h and words_f8_h must not be NULL");
+  try {
+    int64_t off = 0;
+    for (int32_t s = 0; s < batch; ++s) {
+      const SeqGeo geo = geometry(cu_seqlens_h[s + 1] - cu_seqlens_h[s]);
+      const std::vector<Group> order = template_order(geo, tmpl, seed);
+      const int64_t n = (int64_t)order.size();
+      const int64_t n8 = (int8_bp * n + 5000) / 10000;
+      const int64_t nboth = ((int64_t)(int8_bp + fp8_bp) * n + 5000) / 10000;
+      std::vector<uint64_t> w8(geo.Tm, 0), wf(geo.Tm, 0);
+      for (int64_t i = n - n8; i < n; ++i) w8[order[i].r] |= 1ull << order[i].G;
+      for (int64_t i = n - nboth; i < n - n8; ++i) wf[order[i].r] |= 1ull << order[i].G;
+      for (int32_t h = 0; h < num_kv_heads; ++h) {
+        std::memcpy(words_i8_h + h * total_tm + off, w8.data(), geo.Tm * sizeof(uint64_t));
+        std::memcpy(words_f8_h + h * total_tm + off, wf.data(), geo.Tm * sizeof(uint64_t));
+      }
+      off += geo.Tm;
+      if (g_h) g_h[s] = (int32_t)geo.g;
+      if (int8_groups_h) int8_groups_h[s] = n8;
+      if (fp8_groups_h) fp8_groups_h[s] = nboth - n8;
+      if (legal_groups_h) legal_groups_h[s] = n;
+    }
+  } catch (const std::exception& e) {
+    return fail(TILEMIX_EINVAL, "routing build failed: %s", e.what());
+  }
+  return TILEMIX_OK;
+}
+
 int tilemix_build_routing_adaptive(const int32_t* cu_seqlens_h, int32_t batch, int32_t num_kv_heads,
                                    const float* importance_h, int32_t coverage_bp, uint64_t* words_h,
                                    int32_t* g_h, int64_t* int8_groups_h, int64_t* legal_groups_h) {

@@ -37,6 +37,7 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int16v __attribute__((ext_vector_type(16)));
+typedef int int8v __attribute__((ext_vector_type(8)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -153,6 +154,94 @@ __global__ __launch_bounds__(kThreads) void quantize_qk_kernel(QuantArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// FP8 (E4M3) blockwise quantiser: the same blocks, s = fl32(absmax / 448),
+// code = E4M3 round-half-even of fl32(x / s) (the hardware conversion rounds
+// to nearest even and |x / s| <= 448); an all-zero block has s = 0 and codes
+// 0.
+// --------------------------------------------------------------------------
+template <int D, int BLK>
+__device__ inline void quantize_block_fp8(const _Float16* src, uint8_t* dst, float* scale_out, int row_stride,
+                                          int nrows, float* red) {
+  constexpr int kChunksPerRow = D / 8;
+  constexpr int kPerThread = BLK * kChunksPerRow / kThreads;
+  const int tid = threadIdx.x;
+  half8 vals[kPerThread];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / kChunksPerRow, cc = idx % kChunksPerRow;
+    half8 v = {};
+    if (r < nrows) v = *reinterpret_cast<const half8*>(src + (size_t)r * row_stride + cc * 8);
+    vals[i] = v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)v[j]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(amax, 448.0f);
+  if (tid == 0) *scale_out = s;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / kChunksPerRow, cc = idx % kChunksPerRow;
+    if (r >= nrows) continue;
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = amax > 0.f ? __fdiv_rn((float)vals[i][j], s) : 0.f;
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+    *reinterpret_cast<uint2*>(dst + (size_t)r * row_stride + cc * 8) = make_uint2((uint32_t)lo, (uint32_t)hi);
+  }
+}
+
+struct QuantFp8Args {
+  const int32_t* plan;
+  const _Float16* q;
+  const _Float16* k;
+  uint8_t* qf8;
+  uint8_t* kf8;
+  float* qs;
+  float* ks;
+  int32_t hq, hkv, batch, tq, tk;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void quantize_qk_fp8_kernel(QuantFp8Args a) {
+  __shared__ float red[4];
+  const int32_t* seqtab = a.plan + kHeaderLen;
+  int bid = blockIdx.x;
+  const int nq = a.tq * a.hq;
+  if (bid < nq) {
+    const int tile = bid / a.hq, head = bid % a.hq;
+    const int s = find_seq(seqtab, a.batch, kSeqQtOff, tile);
+    const int32_t* rec = seqtab + s * kSeqStride;
+    const int local = tile - rec[kSeqQtOff];
+    const int row0 = rec[kSeqStart] + local * kBlockM;
+    const int nrows = min(kBlockM, rec[kSeqLen] - local * kBlockM);
+    const size_t base = ((size_t)row0 * a.hq + head) * D;
+    quantize_block_fp8<D, kBlockM>(a.q + base, a.qf8 + base, a.qs + (size_t)head * a.tq + tile, a.hq * D,
+                                   nrows, red);
+  } else {
+    bid -= nq;
+    const int tile = bid / a.hkv, head = bid % a.hkv;
+    const int s = find_seq(seqtab, a.batch, kSeqKtOff, tile);
+    const int32_t* rec = seqtab + s * kSeqStride;
+    const int local = tile - rec[kSeqKtOff];
+    const int row0 = rec[kSeqStart] + local * kBlockN;
+    const int nrows = min(kBlockN, rec[kSeqLen] - local * kBlockN);
+    const size_t base = ((size_t)row0 * a.hkv + head) * D;
+    quantize_block_fp8<D, kBlockN>(a.k + base, a.kf8 + base, a.ks + (size_t)head * a.tk + tile, a.hkv * D,
+                                   nrows, red);
+  }
+}
+
+// --------------------------------------------------------------------------
 // Fused prefill pieces shared by the kernel and the int32 tile hook.
 //
 // LDS holds two tile buffers (double buffering); a buffer is one K tile
@@ -238,6 +327,7 @@ struct Tile {
   static constexpr int kBuf = kKRegion + V::kBytes;
   static constexpr int kScales = 1024;  // key-tile scales staged per chunk
   static constexpr int kLds = 2 * kBuf + kScales * 4;
+  static constexpr int kLds3 = kLds + kScales * 4;  // + the FP8 key-tile scales
 };
 
 // Combine a value with the same register of lane l ^ 32 (no LDS round trip).
@@ -334,6 +424,36 @@ __device__ inline void qk_tile_f16(const char* sK, const half8* qf, float16v acc
   TM_FENCE();
 }
 
+// FP8 (E4M3) path of the same block: S^T = K_f8 . Q_f8^T, fp32 accumulation
+// (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales).  A lane holds
+// 32 consecutive codes of its row in each 64-wide step, for K and Q alike.
+template <int D>
+__device__ inline void qk_tile_f8(const char* sK, const int8v* qc, float16v acc[2]) {
+  using K8 = typename Tile<D>::K8;
+  constexpr int kSteps = D / 64;               // per 32-key block
+  const int lane = threadIdx.x & 63, c = lane & 31, hh = lane >> 5;
+  const char* base = sK + K8::at(c, hh * 32);
+  int8v kf[2 * kSteps];
+#pragma unroll
+  for (int step = 0; step < 2 * kSteps; ++step) {
+    const int kb = step / kSteps, kk = step % kSteps;
+    const char* p = base + K8::at(kb * 32, kk * 64);
+    const int4v lo = *reinterpret_cast<const int4v*>(p);
+    const int4v hi = *reinterpret_cast<const int4v*>(p + 16);
+    kf[step] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  TM_FENCE();
+  acc[0] = (float16v){};
+  acc[1] = (float16v){};
+#pragma unroll
+  for (int step = 0; step < 2 * kSteps; ++step) {
+    const int kb = step / kSteps, kk = step % kSteps;
+    acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[step], qc[kk], acc[kb], 0, 0, 0, 0x7f7f7f7f,
+                                                            0, 0x7f7f7f7f);
+  }
+  TM_FENCE();
+}
+
 // Query fragments of this lane's query row (zeros outside the sequence).
 template <int D>
 __device__ inline void load_q(const _Float16* qrow, const int8_t* q8row, bool valid, half8* qf,
@@ -380,6 +500,13 @@ struct PrefillArgs {
   const float* ks;
   const uint64_t* words;
   _Float16* out;
+  // third path (FP8): codes, scales and the FP8 routing words (unused by the
+  // two-path kernel)
+  const uint8_t* qf8;
+  const uint8_t* kf8;
+  const float* qsf8;
+  const float* ksf8;
+  const uint64_t* wordsf8;
   int32_t hq, hkv, tq, tk;
 };
 
@@ -391,13 +518,18 @@ struct RowState {
   float16v o[D / 32];
 };
 
-template <int D, bool kMasked>
-__device__ __forceinline__ void tile_step(const char* buf, int bit, float f_i8, float f16s, const half8* qf,
-                                          const int4v* qb, RowState<D>& st, int k0, int qi, int L) {
+// code: 0 FP16, 1 INT8, 2 FP8 (the FP8 arm exists only with kThree).
+template <int D, bool kMasked, bool kThree>
+__device__ __forceinline__ void tile_step(const char* buf, int code, float f_i8, float f16s, const half8* qf,
+                                          const int4v* qb, const int8v* qc, float f_f8, RowState<D>& st,
+                                          int k0, int qi, int L) {
   const int lane = threadIdx.x & 63, hh = lane >> 5;
   float16v accv[2];
   float f;
-  if (bit) {
+  if (kThree && code == 2) {
+    qk_tile_f8<D>(buf, qc, accv);
+    f = f_f8;
+  } else if (code) {
     int16v acc[2];
     qk_tile_i8<D>(buf, qb, acc);
     f = f_i8;
@@ -501,7 +633,9 @@ __device__ __forceinline__ void tile_step(const char* buf, int bit, float f_i8, 
   TM_FENCE();
 }
 
-template <int D>
+// kThree adds the FP8 path: a second word per (KV head, row) marks FP8
+// groups (never also INT8); without it the kernel is the two-path one.
+template <int D, bool kThree>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   using T = Tile<D>;
@@ -517,6 +651,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int q0 = row * kBlockM;
   const int last_tile = min(q0 + kBlockM - 1, L - 1) / kBlockN;
   const uint64_t word = a.words[(size_t)kv * a.tq + qt_off + row];
+  const uint64_t wordf = kThree ? a.wordsf8[(size_t)kv * a.tq + qt_off + row] : 0ull;
 
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -527,28 +662,48 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const char* kseq = reinterpret_cast<const char*>(a.k + ((size_t)start * a.hkv + kv) * D);
   const char* k8seq = reinterpret_cast<const char*>(a.ki8 + ((size_t)start * a.hkv + kv) * D);
   const char* vseq = reinterpret_cast<const char*>(a.v + ((size_t)start * a.hkv + kv) * D);
+  const char* kf8seq = kThree ? reinterpret_cast<const char*>(a.kf8 + ((size_t)start * a.hkv + kv) * D) : nullptr;
   const int lo16 = T::K16::lane_src(lane, s16), lo8 = T::K8::lane_src(lane, s8);
   const int lov = T::V::lane_src(lane, s16);
 
-  // Routing bit of tile t: (word >> (t / g)) & 1, tracked incrementally.
+  // Routing code of tile t's group G = t / g (tracked incrementally): 1 INT8
+  // when (word >> G) & 1, else 2 FP8 when (wordf >> G) & 1, else 0 FP16.
   int grp = 0, in_grp = 0;  // group of the current tile, position in it
-  auto issue = [&](int t, int bit, char* buf) {
+  auto code_of = [&](int G) {
+    return ((word >> G) & 1ull) ? 1 : (kThree && ((wordf >> G) & 1ull)) ? 2 : 0;
+  };
+  auto issue = [&](int t, int code, char* buf) {
     const int nvalid = min(kBlockN, L - t * kBlockN);
-    if (bit) T::K8::issue(buf, k8seq + (size_t)t * kBlockN * s8, s8, nvalid, w, lane, lo8);
+    if (code == 1) T::K8::issue(buf, k8seq + (size_t)t * kBlockN * s8, s8, nvalid, w, lane, lo8);
+    else if (kThree && code == 2) T::K8::issue(buf, kf8seq + (size_t)t * kBlockN * s8, s8, nvalid, w, lane, lo8);
     else T::K16::issue(buf, kseq + (size_t)t * kBlockN * s16, s16, nvalid, w, lane, lo16);
     T::V::issue(buf + T::kKRegion, vseq + (size_t)t * kBlockN * s16, s16, nvalid, w, lane, lov);
   };
-  issue(0, (int)(word & 1ull), smem);
+  issue(0, code_of(0), smem);
 
   half8 qf[D / 16];
   int4v qb[D / 32];
   load_q<D>(a.q + ((size_t)(start + qi) * a.hq + head) * D,
             a.qi8 + ((size_t)(start + qi) * a.hq + head) * D, qvalid, qf, qb);
+  int8v qc[kThree ? D / 64 : 1];  // FP8 query codes: 32 per lane per 64-wide step
+  if (kThree) {
+    const uint8_t* qrow = a.qf8 + ((size_t)(start + qi) * a.hq + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) {
+      int4v lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+      if (qvalid) {
+        lo = *reinterpret_cast<const int4v*>(qrow + kk * 64 + (lane >> 5) * 32);
+        hi = *reinterpret_cast<const int4v*>(qrow + kk * 64 + (lane >> 5) * 32 + 16);
+      }
+      qc[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
   // Let the compiler see the query loads complete here: it does not count the
   // asm-issued tile loads, so a wait it placed later for these would also
   // wait for every tile load in flight.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   const float sq = load_uniform(a.qs + (size_t)head * a.tq + qt_off + row);
+  const float sqf = kThree ? load_uniform(a.qsf8 + (size_t)head * a.tq + qt_off + row) : 0.f;
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
   const float scale16 = inv_sqrt_d * kLog2e;
   // The row's key-tile scales go through LDS (1024 tiles per chunk): a scalar
@@ -556,9 +711,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // latency.
   const float* kscale = a.ks + (size_t)kv * a.tk + kt_off;
   float* sks = reinterpret_cast<float*>(smem + 2 * T::kBuf);
+  const float* kscalef = kThree ? a.ksf8 + (size_t)kv * a.tk + kt_off : nullptr;
+  float* sksf = sks + T::kScales;  // (FP8 scales, three-path kernel only)
   auto stage_scales = [&](int t0) {
     const int n = min(T::kScales, last_tile + 1 - t0);
     for (int i = tid; i < n; i += kThreads) sks[i] = kscale[t0 + i];
+    if (kThree)
+      for (int i = tid; i < n; i += kThreads) sksf[i] = kscalef[t0 + i];
   };
   stage_scales(0);
 
@@ -571,7 +730,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // One pipelined step: wait for tile t, start tile t+1, compute tile t.
   auto step = [&](int t, auto masked) {
     char* buf = smem + (t & 1) * T::kBuf;
-    const int bit = (int)((word >> grp) & 1ull);
+    const int code = code_of(grp);
     const int ngrp = (in_grp + 1 == g) ? grp + 1 : grp;
     in_grp = (in_grp + 1 == g) ? 0 : in_grp + 1;
     wait_tile_loads();
@@ -580,10 +739,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       stage_scales(t);
       __syncthreads();
     }
-    if (t < last_tile) issue(t + 1, (int)((word >> ngrp) & 1ull), smem + ((t + 1) & 1) * T::kBuf);
+    if (t < last_tile) issue(t + 1, code_of(ngrp), smem + ((t + 1) & 1) * T::kBuf);
     grp = ngrp;
     const float f_i8 = (sq * sks[t & (T::kScales - 1)]) * inv_sqrt_d * kLog2e;
-    tile_step<D, decltype(masked)::value>(buf, bit, f_i8, scale16, qf, qb, st, t * kBlockN, qi, L);
+    const float f_f8 = kThree ? (sqf * sksf[t & (T::kScales - 1)]) * inv_sqrt_d * kLog2e : 0.f;
+    tile_step<D, decltype(masked)::value, kThree>(buf, code, f_i8, scale16, qf, qb, qc, f_f8, st, t * kBlockN,
+                                                  qi, L);
   };
   // Tiles t < 2 row lie entirely below the diagonal of every query of the
   // work unit and inside the sequence: no mask.  The rest (the diagonal
@@ -737,6 +898,11 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
   a.ks = k_scale;
   a.words = words_d;
   a.out = static_cast<_Float16*>(out_f16);
+  a.qf8 = nullptr;
+  a.kf8 = nullptr;
+  a.qsf8 = nullptr;
+  a.ksf8 = nullptr;
+  a.wordsf8 = nullptr;
   a.hq = plan_h[kHq];
   a.hkv = plan_h[kHkv];
   a.tq = plan_h[kTotalQTiles];
@@ -744,11 +910,100 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const unsigned grid = (unsigned)plan_h[kNumItems];
   if (plan_h[kHeadDim] == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3(grid), dim3(kThreads), Tile<64>::kLds, st, a);
+    hipLaunchKernelGGL((prefill_kernel<64, false>), dim3(grid), dim3(kThreads), Tile<64>::kLds, st, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3(grid), dim3(kThreads), Tile<128>::kLds, st, a);
+    hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(grid), dim3(kThreads), Tile<128>::kLds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return TILEMIX_OK;
+}
+
+int tilemix_quantize_qk_fp8(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                            const void* k_f16, uint8_t* q_f8, uint8_t* k_f8, float* q_scale_f8,
+                            float* k_scale_f8, void* hip_stream) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const bool any = plan_h[kTotalTokens] > 0;
+  if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
+      (rc = check_dev_ptr(k_f16, "k_f16", any)) || (rc = check_dev_ptr(q_f8, "q_f8", any)) ||
+      (rc = check_dev_ptr(k_f8, "k_f8", any)) || (rc = check_dev_ptr(q_scale_f8, "q_scale_f8", any)) ||
+      (rc = check_dev_ptr(k_scale_f8, "k_scale_f8", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  QuantFp8Args a;
+  a.plan = plan_d;
+  a.q = static_cast<const _Float16*>(q_f16);
+  a.k = static_cast<const _Float16*>(k_f16);
+  a.qf8 = q_f8;
+  a.kf8 = k_f8;
+  a.qs = q_scale_f8;
+  a.ks = k_scale_f8;
+  a.hq = plan_h[kHq];
+  a.hkv = plan_h[kHkv];
+  a.batch = plan_h[kBatch];
+  a.tq = plan_h[kTotalQTiles];
+  a.tk = plan_h[kTotalKTiles];
+  const int64_t blocks = (int64_t)a.tq * a.hq + (int64_t)a.tk * a.hkv;
+  if (blocks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (plan_h[kHeadDim] == 64)
+    hipLaunchKernelGGL(quantize_qk_fp8_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(quantize_qk_fp8_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
+  return TILEMIX_OK;
+}
+
+int tilemix_prefill_varlen3(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                            const void* k_f16, const void* v_f16, const int8_t* q_i8, const int8_t* k_i8,
+                            const float* q_scale, const float* k_scale, const uint8_t* q_f8,
+                            const uint8_t* k_f8, const float* q_scale_f8, const float* k_scale_f8,
+                            const uint64_t* words_i8_d, const uint64_t* words_f8_d, void* out_f16,
+                            void* hip_stream) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const bool any = plan_h[kNumItems] > 0;
+  if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
+      (rc = check_dev_ptr(k_f16, "k_f16", any)) || (rc = check_dev_ptr(v_f16, "v_f16", any)) ||
+      (rc = check_dev_ptr(q_i8, "q_i8", any)) || (rc = check_dev_ptr(k_i8, "k_i8", any)) ||
+      (rc = check_dev_ptr(q_scale, "q_scale", any)) || (rc = check_dev_ptr(k_scale, "k_scale", any)) ||
+      (rc = check_dev_ptr(q_f8, "q_f8", any)) || (rc = check_dev_ptr(k_f8, "k_f8", any)) ||
+      (rc = check_dev_ptr(q_scale_f8, "q_scale_f8", any)) || (rc = check_dev_ptr(k_scale_f8, "k_scale_f8", any)) ||
+      (rc = check_dev_ptr(words_i8_d, "words_i8_d", any)) || (rc = check_dev_ptr(words_f8_d, "words_f8_d", any)) ||
+      (rc = check_dev_ptr(out_f16, "out_f16", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  PrefillArgs a;
+  a.plan = plan_d;
+  a.q = static_cast<const _Float16*>(q_f16);
+  a.k = static_cast<const _Float16*>(k_f16);
+  a.v = static_cast<const _Float16*>(v_f16);
+  a.qi8 = q_i8;
+  a.ki8 = k_i8;
+  a.qs = q_scale;
+  a.ks = k_scale;
+  a.words = words_i8_d;
+  a.out = static_cast<_Float16*>(out_f16);
+  a.qf8 = q_f8;
+  a.kf8 = k_f8;
+  a.qsf8 = q_scale_f8;
+  a.ksf8 = k_scale_f8;
+  a.wordsf8 = words_f8_d;
+  a.hq = plan_h[kHq];
+  a.hkv = plan_h[kHkv];
+  a.tq = plan_h[kTotalQTiles];
+  a.tk = plan_h[kTotalKTiles];
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const unsigned grid = (unsigned)plan_h[kNumItems];
+  if (plan_h[kHeadDim] == 64)
+    hipLaunchKernelGGL((prefill_kernel<64, true>), dim3(grid), dim3(kThreads), Tile<64>::kLds3, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(grid), dim3(kThreads), Tile<128>::kLds3, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "prefill3 launch");
   return TILEMIX_OK;
 }
 

@@ -142,6 +142,18 @@ def test_errors_are_reported():
                                    None) == -2
 
 
+@pytest.mark.parametrize("template", oracle.TEMPLATES)
+def test_three_class_routing_bit_exact_with_oracle(template):
+    for lens in ([256], [1024, 300, 1, 0, 4160]):
+        cu = synth.cu_seqlens_of(lens)
+        for c8, cf in [(0, 0), (2500, 2500), (5000, 5000), (0, 10000), (7500, 2500), (1000, 0)]:
+            got = tm.tilemix_build_routing3(cu, 2, template, c8, cf, 3)
+            want = oracle.routing_words3(lens, 2, template, c8, cf, 3)
+            assert all(np.array_equal(x, y) for x, y in zip(got, want)), (lens, c8, cf)
+    with pytest.raises(tm.TileMixError, match="int8_bp"):
+        tm.tilemix_build_routing3(synth.cu_seqlens_of([256]), 1, template, 6000, 5000)
+
+
 @pytest.mark.parametrize("lens,hkv", [([256], 1), ([1024, 300, 1, 0, 129], 3), ([4160, 8192], 2)])
 def test_adaptive_routing_bit_exact_with_oracle(lens, hkv):
     geos = [oracle.seq_geometry(L) for L in lens]

@@ -1,0 +1,183 @@
+"""Parity of the FP8 (E4M3) third path (HIP, through the C ABI) with the
+oracle: FP8 codes and scales bit-exact, three-path prefill output within the
+fp16 tolerance, and identical to the two-path kernel when no group is FP8."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import mixed_precision_attention_amd as tm
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+MAX_ABS = 4e-3
+MEAN_ABS = 5e-4
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def run3(q, k, v, cu, hq, hkv, template, c8, cf, seed=0):
+    d = q.shape[2]
+    tp = tm.TileMixPrefill3(cu, hq, hkv, d, template, c8, cf, seed)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    out = torch.full_like(qd, float("nan"))
+    tp(qd, kd, vd, out)
+    torch.cuda.synchronize()
+    T = q.shape[0]
+    return tp, out.cpu().numpy(), dict(
+        q_f8=tp.q_f8.cpu().numpy()[:T], k_f8=tp.k_f8.cpu().numpy()[:T],
+        q_scale_f8=tp.q_scale_f8.cpu().numpy()[:, :tp.tq], k_scale_f8=tp.k_scale_f8.cpu().numpy()[:, :tp.tk],
+        q_i8=tp.q_i8.cpu().numpy()[:T], k_i8=tp.k_i8.cpu().numpy()[:T],
+        q_scale=tp.q_scale.cpu().numpy()[:, :tp.tq], k_scale=tp.k_scale.cpu().numpy()[:, :tp.tk])
+
+
+def oracle3(q, k, v, cu, hq, hkv, tp, rows=None):
+    q_i8, qs = oracle.quantize_blocks(q, cu, 128)
+    k_i8, ks = oracle.quantize_blocks(k, cu, 64)
+    qf, qfs = oracle.quantize_blocks_fp8(q, cu, 128)
+    kf, kfs = oracle.quantize_blocks_fp8(k, cu, 64)
+    return oracle.prefill_attention3(q, k, v, q_i8, k_i8, qs, ks, qf, kf, qfs, kfs, tp.words, tp.words_f8,
+                                     cu, hq, hkv, rows=rows)
+
+
+def assert_close(got, ref):
+    got = got.astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    assert err.max() <= MAX_ABS, f"max abs err {err.max():.3e}"
+    assert err.mean() <= MEAN_ABS, f"mean abs err {err.mean():.3e}"
+
+
+# The FP8 matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4) sums each
+# 64-product step with about 12 bits relative to the step's largest product
+# (measured: at most 2^-11.5 of it, for products spanning the whole E4M3
+# range), not to fp32.  On an FP8 tile the score error is therefore bounded
+# by EPS * sum over steps of max |q8 k8| * s_q s_k / sqrt(d), with EPS =
+# 2^-10.5 (twice the largest measured); a row's softmax output moves by at
+# most exp(2 delta) - 1 times max |V| for a score error delta.
+EPS_F8 = 2.0 ** -10.5
+
+
+def fp8_row_bound(q, k, v, cu, hq, hkv, tp, rows_sel):
+    """Per output row, the bound above: max over its FP8 tiles' scores."""
+    qf, qfs = oracle.quantize_blocks_fp8(q, cu, 128)
+    kf, kfs = oracle.quantize_blocks_fp8(k, cu, 64)
+    qv, kv_ = oracle.fp8_e4m3_decode(qf), oracle.fp8_e4m3_decode(kf)
+    d = q.shape[2]
+    grp = hq // hkv
+    bound = np.zeros((q.shape[0], hq))
+    lens = np.diff(cu)
+    qt = np.concatenate([[0], np.cumsum([-(-int(L) // 128) for L in lens])])
+    kt = np.concatenate([[0], np.cumsum([-(-int(L) // 64) for L in lens])])
+    for s, L in enumerate(lens):
+        L = int(L)
+        if L == 0:
+            continue
+        geo = oracle.seq_geometry(L)
+        for h in range(hq):
+            kvh = h // grp
+            for i in range(L):
+                if rows_sel is not None and (s, i) not in rows_sel:
+                    continue
+                r = i // 128
+                wf = int(tp.words_f8[kvh, qt[s] + r])
+                w8 = int(tp.words[kvh, qt[s] + r])
+                delta = 0.0
+                for t in range(i // 64 + 1):
+                    G = t // geo.g
+                    if not ((wf >> G) & 1) or ((w8 >> G) & 1):
+                        continue
+                    j0, j1 = 64 * t, min(64 * t + 64, i + 1)
+                    prod = np.abs(qv[cu[s] + i, h][None, :] * kv_[cu[s] + j0:cu[s] + j1, kvh])
+                    steps = prod.reshape(j1 - j0, -1, 64).max(axis=2).sum(axis=1)
+                    scale = float(qfs[h, qt[s] + r]) * float(kfs[kvh, kt[s] + t]) / np.sqrt(d)
+                    delta = max(delta, EPS_F8 * steps.max() * scale)
+                vmax = np.abs(v[cu[s]:cu[s] + i + 1, kvh].astype(np.float64)).max()
+                bound[cu[s] + i, h] = (np.exp(2 * delta) - 1) * vmax
+    return bound
+
+
+def assert_close_f8(got, ref, bound):
+    got = got.astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref).max(axis=2)
+    excess = err - (MAX_ABS + bound)
+    assert excess.max() <= 0, f"max abs err {err.max():.3e}, worst excess {excess.max():.3e}"
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d", [([256], 1, 1, 64), ([300, 77, 0, 129, 1, 64], 4, 2, 64),
+                                           ([1024, 513], 6, 2, 128)])
+def test_fp8_quantizer_bit_exact(lens, hq, hkv, d):
+    _log(f"fp8 quantizer lens={lens} d={d}")
+    q, k, v, cu = synth.make_qkv(lens, hq, hkv, d, outliers=True, seed=51)
+    tp, out, g = run3(q, k, v, cu, hq, hkv, "band", 2500, 2500)
+    oq, oqs = oracle.quantize_blocks_fp8(q, cu, 128)
+    ok, oks = oracle.quantize_blocks_fp8(k, cu, 64)
+    assert np.array_equal(g["q_f8"], oq) and np.array_equal(g["k_f8"], ok)
+    assert np.array_equal(g["q_scale_f8"].view(np.uint32), oqs.view(np.uint32))
+    assert np.array_equal(g["k_scale_f8"].view(np.uint32), oks.view(np.uint32))
+
+
+@pytest.mark.parametrize("template,c8,cf,d", [("band", 0, 10000, 64), ("sptrans", 2500, 5000, 128),
+                                              ("rowrandom", 5000, 2500, 64), ("global", 0, 5000, 128),
+                                              ("bigbird", 3000, 3000, 128)])
+def test_three_path_varlen(template, c8, cf, d):
+    # N(0,1) inputs: the FP8 accumulation error is far below the fp16 bar
+    lens, hq, hkv = [300, 77, 0, 129, 1, 64, 700], 6, 2
+    _log(f"three-path {template} c8={c8} cf={cf} d={d}")
+    q, k, v, cu = synth.make_qkv(lens, hq, hkv, d, outliers=False, seed=52)
+    tp, out, _ = run3(q, k, v, cu, hq, hkv, template, c8, cf)
+    assert_close(out, oracle3(q, k, v, cu, hq, hkv, tp))
+
+
+@pytest.mark.parametrize("cf,d", [(10000, 64), (5000, 128)])
+def test_three_path_outlier_channels(cf, d):
+    # outlier channels: blocks dominated by a few large products, where the
+    # FP8 instruction's accumulation error is visible; held to the derived bound
+    lens, hq, hkv = [300, 129], 2, 1
+    _log(f"three-path outliers cf={cf} d={d}")
+    q, k, v, cu = synth.make_qkv(lens, hq, hkv, d, outliers=True, seed=58)
+    tp, out, _ = run3(q, k, v, cu, hq, hkv, "band", 0, cf)
+    ref = oracle3(q, k, v, cu, hq, hkv, tp)
+    assert_close_f8(out, ref, fp8_row_bound(q, k, v, cu, hq, hkv, tp, None))
+
+
+def test_three_path_long_rows_g2():
+    lens, hq, hkv, d = [4160], 2, 1, 128
+    _log("three-path L=4160")
+    q, k, v, cu = synth.make_qkv(lens, hq, hkv, d, outliers=False, seed=53)
+    tp, out, _ = run3(q, k, v, cu, hq, hkv, "sptrans", 2500, 5000)
+    rows = [(0, h, r) for h in range(hq) for r in (0, 16, 32)]
+    ref = oracle3(q, k, v, cu, hq, hkv, tp, rows=rows)
+    sel = np.concatenate([np.arange(128 * r, min(128 * r + 128, 4160)) for r in (0, 16, 32)])
+    assert_close(out[sel], ref[sel])
+
+
+def test_three_path_without_fp8_equals_two_path():
+    lens, hq, hkv, d = [1024, 300], 6, 2, 128
+    _log("three-path with no FP8 groups vs two-path kernel")
+    q, k, v, cu = synth.make_qkv(lens, hq, hkv, d, outliers=True, seed=54)
+    tp3, out3, _ = run3(q, k, v, cu, hq, hkv, "sptrans", 7500, 0)
+    tp = tm.TileMixPrefill(cu, hq, hkv, d, "sptrans", 7500)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    out2 = tp(qd, kd, vd).cpu().numpy()
+    assert np.array_equal(out3, out2)
+
+
+def test_fp8_lossless_inputs_give_plain_attention():
+    lens, hq, hkv, d = [300, 129], 2, 1, 128
+    _log("fp8 lossless inputs")
+    cu = synth.cu_seqlens_of(lens)
+    q = synth.lossless_blocks_fp8(lens, hq, d, 128, seed=55)
+    k = synth.lossless_blocks_fp8(lens, hkv, d, 64, seed=56)
+    _, _, v, _ = synth.make_qkv(lens, hq, hkv, d, outliers=False, seed=57)
+    tp, out, _ = run3(q, k, v, cu, hq, hkv, "band", 0, 10000)
+    from independent import naive_causal_attention
+    ref = naive_causal_attention(q, k, v, cu, hq, hkv)
+    assert_close_f8(out, ref, fp8_row_bound(q, k, v, cu, hq, hkv, tp, None))
