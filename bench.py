@@ -15,6 +15,10 @@ fp16-equivalent TFLOP/s (INT8 operations weighted by the fp16/int8 peak
 ratio) against the published MI355X dense fp16 MFMA peak, i.e. ``frac`` is
 the coverage-weighted MFMA roofline time over the measured kernel time.
 
+``fp8`` (skip with --no-fp8) times the three-path prefill (FP16 / FP8 / INT8
+groups from the same template) at two coverage mixes, against the
+three-precision MFMA roofline.
+
 ``adaptive`` (skip with --no-adaptive) times the content-dependent routing
 statistic, the host ranking, and the prefill under the resulting words at the
 same coverage.
@@ -39,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16 = 2.5e15   # MI355X dense fp16 MFMA, FLOP/s (published)
 PEAK_I8 = 5.0e15    # MI355X dense int8 MFMA, OP/s (published)
+PEAK_F8 = 5.0e15    # MI355X dense fp8 MFMA, FLOP/s (published)
 PEAK_HBM = 8.0e12   # MI355X HBM3E, bytes/s (published)
 METRIC = "prefill attn tokens/s + % of MFMA roofline, 3B shape L=4k B=8 SpTrans75"
 KERNEL_SRC = os.path.join(ROOT, "mixed_precision_attention_amd", "csrc", "tilemix_kernels.hip")
@@ -171,6 +176,44 @@ def bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, steps):
                                     "algorithmic_bytes": imp_bytes},
             "route_total_ms": route_ms, "prefill_ms": attn_ms, "frac": t_roof / (attn_ms * 1e-3),
             "int8_pair_share": P8 / P}
+
+
+def bench_fp8(qd, kd, vd, cu, hq, hkv, d, template, mixes, steps):
+    """Three-path prefill (FP16 / FP8 / INT8 groups) at the given (INT8, FP8)
+    coverages: FP8 quantiser time and the prefill kernel against the
+    three-precision MFMA roofline (FP8 at the published dense peak)."""
+    import torch
+    import mixed_precision_attention_amd as tm
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(qd)
+    rows = []
+    for c8, cf in mixes:
+        tp = tm.TileMixPrefill3(cu, hq, hkv, d, template, c8, cf)
+        tp.quantize(qd, kd)
+        for _ in range(3):
+            tp.attend(qd, kd, vd, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            tm.tilemix_quantize_qk_fp8(tp.plan_h, tp.plan_d, qd, kd, tp.q_f8, tp.k_f8, tp.q_scale_f8,
+                                       tp.k_scale_f8)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        q8_us = e0.elapsed_time(e1) * 1e3 / steps
+        e0.record(stream)
+        for _ in range(steps):
+            tp.attend(qd, kd, vd, out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
+        _, Pf = legal_pair_counts(cu, tp.words_f8, hq, hkv)
+        t_roof = 2 * d * (P - P8 - Pf) / PEAK_F16 + 2 * d * P8 / PEAK_I8 + 2 * d * Pf / PEAK_F8 \
+            + 2 * d * P / PEAK_F16
+        rows.append({"int8_bp": c8, "fp8_bp": cf, "prefill_ms": ms, "frac": t_roof / (ms * 1e-3),
+                     "int8_pair_share": P8 / P, "fp8_pair_share": Pf / P, "fp8_quantize_us": q8_us})
+    return {"template": template, "runs": rows}
 
 
 def decode_bytes(cu, hq, hkv, d, tq, tk):
@@ -332,6 +375,8 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode step over the INT8 key/value cache")
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the three-path (FP16/FP8/INT8) prefill leg")
     ap.add_argument("--no-adaptive", action="store_true",
                     help="skip the adaptive-routing leg (importance statistic + prefill under its words)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -454,6 +499,8 @@ def main(argv=None):
                       "roofline_us": t_roof * 1e6, "host_build_ms": host_build_ms,
                       "wall_s": wall},
     }
+    if not args.no_fp8:
+        result["fp8"] = bench_fp8(qd, kd, vd, cu, hq, hkv, d, template, [(5000, 2500), (0, 7500)], 20)
     if not args.no_adaptive:
         result["adaptive"] = bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, 20)
     if not args.no_decode:
