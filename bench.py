@@ -91,11 +91,13 @@ def traffic_record(path):
 
 def _counter_mean_kib(path, kernel_substr):
     """Mean per-dispatch value (KiB) of the one counter in a rocprofv3
-    counter_collection.csv, over dispatches whose name contains the text."""
+    counter_collection.csv, over dispatches whose name contains the text
+    (every piece of it, when it is a tuple)."""
     import csv
+    parts = kernel_substr if isinstance(kernel_substr, tuple) else (kernel_substr,)
     per = {}
     for r in csv.DictReader(open(path)):
-        if kernel_substr in r["Kernel_Name"]:
+        if all(p in r["Kernel_Name"] for p in parts):
             per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     if not per:
         raise SystemExit(f"no dispatch of {kernel_substr!r} in {path}")
@@ -106,9 +108,11 @@ def write_traffic(args):
     """HBM bytes per prefill launch: FETCH_SIZE and WRITE_SIZE scaled by what
     the same counters read for a plain copy of known size."""
     fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.write_traffic
+    # the two-path kernel only (the FP8 leg's three-path kernel is
+    # prefill_kernel<d, true>)
     kname = "tilemix::prefill_kernel"
-    fetch, nf = _counter_mean_kib(fetch_csv, kname)
-    write, nw = _counter_mean_kib(write_csv, kname)
+    fetch, nf = _counter_mean_kib(fetch_csv, (kname + "<", ", false>"))
+    write, nw = _counter_mean_kib(write_csv, (kname + "<", ", false>"))
     cfetch, _ = _counter_mean_kib(cfetch_csv, "copyBuffer")
     cwrite, _ = _counter_mean_kib(cwrite_csv, "copyBuffer")
     f_scale = args.copy_size / (cfetch * 1024)
