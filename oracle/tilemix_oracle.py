@@ -1,6 +1,8 @@
 """TileMix oracle -- a plain, slow, CPU-only statement of what the fused
-mixed-precision prefill path computes, and of one decode step against an
-INT8 key/value cache.
+mixed-precision prefill path computes, of one decode step against an INT8
+key/value cache, of the FP8 third score path, of content-dependent routing
+words and of a synthetic multi-layer stack that carries the deviation from
+layer to layer.
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or run this module.  It shares
@@ -858,3 +860,111 @@ def prefill_attention3(q, k, v, q_i8, k_i8, q_scale, k_scale, q_f8, k_f8, q_scal
         vf = v[start:start + nk, kv, :].astype(np.float64)
         out[start + q0:start + q1, h, :] = (p @ vf) / p.sum(axis=1, keepdims=True)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Synthetic multi-layer stack: how the deviation grows with depth
+# ---------------------------------------------------------------------------
+#
+# [Explainer, 数字精度混用到底靠不靠谱]: besides the single-layer deviation,
+# the paper's numerical check found that deeper models (32 against 12 layers)
+# pile up more deviation, the error of one layer being carried into the next.
+# The pages name no layer structure beyond attention, so this synthetic
+# analogue keeps only what carries the error from layer to layer: attention
+# whose Q, K and V are computed from the running hidden state, and a residual
+# connection.  Readings taken here:
+#   * the hidden state x [T, Hq*d] splits into Hkv independent streams of
+#     width W = (Hq/Hkv)*d, one per KV head: channels g*W .. g*W+W-1 belong
+#     to KV head g and to its query heads g*Hq/Hkv .. (g+1)*Hq/Hkv - 1;
+#   * a layer is pre-norm attention plus residual, per stream:
+#       u = x_g / sqrt(mean(x_g^2) + eps)             (RMS norm, unit gain)
+#       [q_g | k_g | v_g] = u . Wqkv_g^T              (Wqkv_g: (W+2d) x W)
+#       o = TileMix attention of (q, k, v)            (this module's prefill)
+#       x_g <- x_g + o_g . Wo_g^T                      (Wo_g: W x W);
+#     row n < W of Wqkv_g feeds query head g*Hq/Hkv + n//d, channel n % d;
+#     rows W .. W+d-1 feed k of KV head g and the last d rows its v;
+#   * u, q, k, v and o are stored in binary16 (the attention's operands are
+#     FP16 ([Digest, method])); products accumulate exactly here, and the
+#     residual stream is float64;
+#   * every layer uses the same routing words ([Digest, method]: one static
+#     template is reused across layers);
+#   * the deviation at depth l is the mean absolute difference of the hidden
+#     states of two stacks that differ only in their routing words, against
+#     the stack with no INT8 group.
+
+STACK_EPS = 1e-6
+
+
+def stack_width(hq: int, hkv: int, d: int) -> int:
+    """Channels of one KV head's residual stream."""
+    return (hq // hkv) * d
+
+
+def stack_rms_norm(x, hkv: int, eps: float = STACK_EPS):
+    """u = x / sqrt(mean(x^2) + eps) over each stream's W channels of every
+    token, in float64, rounded once to binary16.  x: [T, Hq*d]."""
+    x = np.asarray(x, dtype=np.float64)
+    T, C = x.shape
+    xg = x.reshape(T, hkv, C // hkv)
+    ms = (xg * xg).mean(axis=2, keepdims=True)
+    return (xg / np.sqrt(ms + eps)).reshape(T, C).astype(np.float16)
+
+
+def stack_qkv(u, wqkv, hq: int, hkv: int, d: int):
+    """q [T, Hq, d], k and v [T, Hkv, d] (binary16) from u [T, Hq*d] and one
+    layer's wqkv [Hkv, W+2d, W]: each output is the exact dot product of u's
+    stream with a row of wqkv, rounded once to binary16."""
+    T = u.shape[0]
+    W = stack_width(hq, hkv, d)
+    ug = np.asarray(u, dtype=np.float64).reshape(T, hkv, W)
+    y = np.einsum("tgk,gnk->tgn", ug, np.asarray(wqkv, dtype=np.float64)).astype(np.float16)
+    q = np.ascontiguousarray(y[:, :, :W].reshape(T, hq, d))
+    k = np.ascontiguousarray(y[:, :, W:W + d])
+    v = np.ascontiguousarray(y[:, :, W + d:])
+    return q, k, v
+
+
+def stack_out_residual(x, o16, wo, hq: int, hkv: int, d: int):
+    """x + o . Wo^T per stream (float64).  o16: binary16 [T, Hq, d] (query
+    head g*Hq/Hkv + j fills stream channels j*d .. j*d+d-1); wo [Hkv, W, W]."""
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    W = stack_width(hq, hkv, d)
+    og = np.asarray(o16, dtype=np.float64).reshape(T, hkv, W)
+    y = np.einsum("tgk,gnk->tgn", og, np.asarray(wo, dtype=np.float64))
+    return x + y.reshape(T, hq * d)
+
+
+def stack_layer(x, wqkv, wo, words, cu_seqlens, hq: int, hkv: int, d: int,
+                eps: float = STACK_EPS, attn_offset=None):
+    """One layer of the stack (module comment above).  ``attn_offset``, when
+    given, is added to the float64 attention output before it is rounded to
+    binary16 (used to propagate a per-layer error bound through the stack)."""
+    cu = [int(c) for c in cu_seqlens]
+    u = stack_rms_norm(x, hkv, eps)
+    q, k, v = stack_qkv(u, wqkv, hq, hkv, d)
+    q_i8, q_scale = quantize_blocks(q, cu, BLOCK_M)
+    k_i8, k_scale = quantize_blocks(k, cu, BLOCK_N)
+    o = prefill_attention(q, k, v, q_i8, k_i8, q_scale, k_scale, words, cu, hq, hkv)
+    if attn_offset is not None:
+        o = o + attn_offset
+    return stack_out_residual(x, o.astype(np.float16), wo, hq, hkv, d)
+
+
+def stack_forward(x0, wqkv, wo, words, cu_seqlens, hq: int, hkv: int, d: int,
+                  eps: float = STACK_EPS, attn_offsets=None):
+    """Hidden states after each layer, a list of float64 [T, Hq*d]; layer l
+    uses wqkv[l] and wo[l] (and ``attn_offsets[l]`` when given)."""
+    xs = []
+    x = np.asarray(x0, dtype=np.float64)
+    for l in range(len(wqkv)):
+        off = None if attn_offsets is None else attn_offsets[l]
+        x = stack_layer(x, wqkv[l], wo[l], words, cu_seqlens, hq, hkv, d, eps, off)
+        xs.append(x)
+    return xs
+
+
+def depth_deviation(xs_a, xs_b):
+    """Mean absolute difference of two stacks' hidden states at each depth."""
+    return np.array([np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).mean()
+                     for a, b in zip(xs_a, xs_b)])

@@ -172,3 +172,27 @@ def lossless_blocks_fp8(seqlens, heads: int, d: int, block: int, seed: int = 0):
             e = rng.integers(4, 10, size=heads).astype(np.float64)
             vals[b0:b1] *= np.exp2(-e)[None, :, None]
     return vals.astype(np.float16)
+
+
+def stack_weights(n_layers: int, hq: int, hkv: int, d: int, seed: int = 0, gain_qk: float = 1.0):
+    """Random weights of a synthetic attention stack: wqkv float16
+    [n_layers, Hkv, W+2d, W] and wo float16 [n_layers, Hkv, W, W], W =
+    (Hq/Hkv)*d.  Entries are N(0, 1/W) in float32 (the q and k rows times
+    ``gain_qk``), drawn layer by layer (wqkv then wo), rounded to float16."""
+    W = (hq // hkv) * d
+    rng = np.random.default_rng(seed)
+    wqkv = np.empty((n_layers, hkv, W + 2 * d, W), dtype=np.float16)
+    wo = np.empty((n_layers, hkv, W, W), dtype=np.float16)
+    sd = np.float32(1.0 / np.sqrt(W))
+    for l in range(n_layers):
+        a = rng.standard_normal((hkv, W + 2 * d, W), dtype=np.float32) * sd
+        a[:, :W + d] *= np.float32(gain_qk)
+        wqkv[l] = a.astype(np.float16)
+        wo[l] = (rng.standard_normal((hkv, W, W), dtype=np.float32) * sd).astype(np.float16)
+    return wqkv, wo
+
+
+def stack_input(tokens: int, hq: int, d: int, seed: int = 0):
+    """Initial hidden state of the stack: float32 N(0, 1), [tokens, Hq*d]."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((tokens, hq * d), dtype=np.float32)
