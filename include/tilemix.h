@@ -258,6 +258,51 @@ int tilemix_routing_importance(const int32_t* plan_h, const int32_t* plan_d, con
                                void* workspace, int64_t workspace_bytes, float* importance_d,
                                void* hip_stream);
 
+/* ---- Synthetic multi-layer stack ------------------------------------------
+ * [Explainer, 数字精度混用到底靠不靠谱]: deeper models pile up more deviation,
+ * the error of one layer being carried into the next.  The pages give no
+ * layer beyond attention; the stack below keeps attention whose Q, K, V come
+ * from the running hidden state, plus a residual connection.  The hidden
+ * state x [T, Hq*d] (fp32) is Hkv independent streams of width
+ * W = (Hq/Hkv)*d: stream g is channels g*W .. g*W+W-1, owned by KV head g
+ * and its query heads g*Hq/Hkv .. (g+1)*Hq/Hkv - 1.  d is 64 or 128 and W at
+ * most 1024.  All pointers are device pointers, 16-byte aligned; nothing is
+ * allocated; kernels run on hip_stream.  Errors: EINVAL (NULL or misaligned
+ * pointer, negative size, Hq not a multiple of Hkv, small workspace),
+ * EUNSUPPORTED (d, W). */
+
+/* u = fl16(x * 1/sqrt(mean(x^2) + eps)) per (token, stream), sum of squares
+ * and the factor in binary32.  x: float [T, Hq*d]; u_f16: [T, Hq*d]. */
+int tilemix_stack_rms_norm(const float* x, void* u_f16, int64_t tokens, int32_t hq, int32_t hkv,
+                           int32_t head_dim, float eps, void* hip_stream);
+
+/* [q | k | v] = u_g . Wqkv_g^T per stream (f16 matrix cores, fp32
+ * accumulation, one rounding to fp16).  wqkv_f16: [Hkv][W + 2d][W], row n of
+ * stream g = the weights of output n: n < W feeds q head g*Hq/Hkv + n/d,
+ * channel n % d; n in [W, W+d) feeds k head g, channel n - W; the last d rows
+ * feed v head g.  Outputs q_f16 [T, Hq, d], k_f16 and v_f16 [T, Hkv, d]. */
+int tilemix_stack_qkv(const void* u_f16, const void* wqkv_f16, void* q_f16, void* k_f16, void* v_f16,
+                      int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim, void* hip_stream);
+
+/* x_g += o_g . Wo_g^T per stream (fp32 accumulation, then one fp32 add).
+ * o_f16: [T, Hq, d] (query head g*Hq/Hkv + j fills stream channels
+ * j*d .. j*d+d-1); wo_f16: [Hkv][W][W], row n = output channel n. */
+int tilemix_stack_out_residual(const void* o_f16, const void* wo_f16, float* x, int64_t tokens,
+                               int32_t hq, int32_t hkv, int32_t head_dim, void* hip_stream);
+
+/* Bytes of device workspace one tilemix_stack_layer call needs for this
+ * plan (normalised input / attention output, Q, K, V, int8 codes and scales). */
+int tilemix_stack_workspace_size(const int32_t* plan_h, int64_t* bytes);
+
+/* One layer in place on x (device float [T, Hq*d], T = the plan's tokens):
+ * tilemix_stack_rms_norm, tilemix_stack_qkv, tilemix_quantize_qk,
+ * tilemix_prefill_varlen with words_d ([Digest, method]: the same template
+ * words serve every layer), tilemix_stack_out_residual.  The workspace's
+ * contents are overwritten; calls that share a workspace must not overlap. */
+int tilemix_stack_layer(const int32_t* plan_h, const int32_t* plan_d, const uint64_t* words_d, float* x,
+                        const void* wqkv_f16, const void* wo_f16, float eps, void* workspace,
+                        int64_t workspace_bytes, void* hip_stream);
+
 /* Test hook (device): the int32 accumulator of one 128 x 64 INT8 score tile
  * (sequence seq, query head, query-tile row r, key tile t), computed by the
  * same device routine the fused kernel uses ([Digest, method]: INT8 MMA with

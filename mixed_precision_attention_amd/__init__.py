@@ -5,8 +5,9 @@ quantisation, fused attention) runs inside libtilemix.so -- the host steps in
 its C++ half, the device steps in its HIP kernels.  PyTorch supplies device
 memory and the current HIP stream.  The functions carry the names of the C
 entry points declared in include/tilemix.h; ``TileMixPrefill`` bundles them
-for one packed batch shape and ``TileMixDecode`` for one decode step over an
-INT8 key/value cache.
+for one packed batch shape, ``TileMixDecode`` for one decode step over an
+INT8 key/value cache and ``TileMixStack`` for a synthetic stack of
+attention + residual layers.
 
 The library must be built first (``python -m mixed_precision_attention_amd.build``);
 importing works without it, but every call raises ``TileMixError`` when the
@@ -63,6 +64,11 @@ _SIGNATURES = {
     "tilemix_routing_importance": ([_P] * 7 + [_I64, _P, _P], ctypes.c_int),
     "tilemix_decode_workspace_size": ([_P, _P], ctypes.c_int),
     "tilemix_decode_varlen": ([_P] * 9 + [_I64, _P, _P], ctypes.c_int),
+    "tilemix_stack_rms_norm": ([_P, _P, _I64, _I32, _I32, _I32, ctypes.c_float, _P], ctypes.c_int),
+    "tilemix_stack_qkv": ([_P] * 5 + [_I64, _I32, _I32, _I32, _P], ctypes.c_int),
+    "tilemix_stack_out_residual": ([_P] * 3 + [_I64, _I32, _I32, _I32, _P], ctypes.c_int),
+    "tilemix_stack_workspace_size": ([_P, _P], ctypes.c_int),
+    "tilemix_stack_layer": ([_P] * 6 + [ctypes.c_float, _P, _I64, _P], ctypes.c_int),
 }
 
 
@@ -287,6 +293,43 @@ def tilemix_decode_varlen(plan_h, plan_d, q, k_i8, v_i8, k_scale, v_scale, words
         _stream(stream)))
 
 
+def tilemix_stack_rms_norm(x, u, hq: int, hkv: int, head_dim: int, eps: float, stream=None):
+    import torch
+    _check(lib().tilemix_stack_rms_norm(
+        _dptr(x, torch.float32, "x"), _dptr(u, torch.float16, "u"), x.shape[0], hq, hkv, head_dim, eps,
+        _stream(stream)))
+
+
+def tilemix_stack_qkv(u, wqkv, q, k, v, hq: int, hkv: int, head_dim: int, stream=None):
+    import torch
+    _check(lib().tilemix_stack_qkv(
+        _dptr(u, torch.float16, "u"), _dptr(wqkv, torch.float16, "wqkv"), _dptr(q, torch.float16, "q"),
+        _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), u.shape[0], hq, hkv, head_dim,
+        _stream(stream)))
+
+
+def tilemix_stack_out_residual(o, wo, x, hq: int, hkv: int, head_dim: int, stream=None):
+    import torch
+    _check(lib().tilemix_stack_out_residual(
+        _dptr(o, torch.float16, "o"), _dptr(wo, torch.float16, "wo"), _dptr(x, torch.float32, "x"),
+        x.shape[0], hq, hkv, head_dim, _stream(stream)))
+
+
+def tilemix_stack_workspace_size(plan_h) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().tilemix_stack_workspace_size(_hptr(plan_h), ctypes.byref(n)))
+    return int(n.value)
+
+
+def tilemix_stack_layer(plan_h, plan_d, words_d, x, wqkv, wo, eps: float, workspace, stream=None):
+    import torch
+    _check(lib().tilemix_stack_layer(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(words_d, torch.int64, "words_d"),
+        _dptr(x, torch.float32, "x"), _dptr(wqkv, torch.float16, "wqkv"), _dptr(wo, torch.float16, "wo"),
+        eps, _dptr(workspace, torch.uint8, "workspace"), workspace.numel() if workspace is not None else 0,
+        _stream(stream)))
+
+
 # ------------------------------------------------------------------ bundle
 
 class TileMixPrefill:
@@ -426,3 +469,55 @@ class TileMixDecode:
         tilemix_decode_varlen(self.plan_h, self.plan_d, q, self.k_i8, self.v_i8, self.k_scale,
                               self.v_scale, self.words_d, self.workspace, out, stream)
         return out
+
+
+class TileMixStack:
+    """A synthetic stack of attention + residual layers over one packed batch
+    shape: the plan and routing words (one template for every layer), the
+    layers' weights on the device and one layer's workspace."""
+
+    def __init__(self, cu_seqlens, hq: int, hkv: int, head_dim: int, template, coverage_bp: int,
+                 seed: int = 0, eps: float = 1e-6, device="cuda"):
+        import torch
+        self.cu = _host_i32(cu_seqlens)
+        self.hq, self.hkv, self.d = hq, hkv, head_dim
+        self.eps = eps
+        self.device = device
+        self.tokens, self.tq, self.tk = tilemix_query_sizes(self.cu)
+        self.plan_h = tilemix_build_plan(self.cu, hq, hkv, head_dim)
+        self.plan_d = torch.from_numpy(self.plan_h).to(device)
+        self.set_routing(template, coverage_bp, seed)
+        self.workspace = torch.empty(max(tilemix_stack_workspace_size(self.plan_h), 16),
+                                     dtype=torch.uint8, device=device)
+        self.wqkv = self.wo = None
+
+    def set_routing(self, template, coverage_bp: int, seed: int = 0):
+        import torch
+        self.words, self.g, self.n_int8, self.n_legal = tilemix_build_routing(
+            self.cu, self.hkv, template, coverage_bp, seed)
+        w = self.words if self.words.size else np.zeros((1, 1), dtype=np.uint64)
+        self.words_d = torch.from_numpy(w.view(np.int64)).to(self.device)
+
+    def set_weights(self, wqkv, wo):
+        """wqkv: fp16 [layers, Hkv, W + 2d, W]; wo: fp16 [layers, Hkv, W, W]
+        (device tensors, kept by reference)."""
+        self.wqkv, self.wo = wqkv, wo
+
+    @property
+    def layers(self) -> int:
+        return 0 if self.wqkv is None else self.wqkv.shape[0]
+
+    def layer(self, x, l: int, stream=None):
+        """Layer l in place on x (fp32 [T, Hq*d])."""
+        tilemix_stack_layer(self.plan_h, self.plan_d, self.words_d, x, self.wqkv[l], self.wo[l], self.eps,
+                            self.workspace, stream)
+
+    def forward(self, x, record=None, stream=None):
+        """Run every layer in place on x; returns {depth: copy of x} for the
+        depths (1-based) listed in ``record``."""
+        snaps = {}
+        for l in range(self.layers):
+            self.layer(x, l, stream)
+            if record is not None and l + 1 in record:
+                snaps[l + 1] = x.clone()
+        return snaps

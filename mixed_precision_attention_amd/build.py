@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libtilemix.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["tilemix_host.cpp", "tilemix_kernels.hip", "tilemix_decode.hip", "tilemix_adaptive.hip"]
+SOURCES = ["tilemix_host.cpp", "tilemix_kernels.hip", "tilemix_decode.hip", "tilemix_adaptive.hip",
+           "tilemix_stack.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.
 HIP_FLAGS = [

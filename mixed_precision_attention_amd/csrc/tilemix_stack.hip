@@ -1,0 +1,404 @@
+// Device half of the synthetic multi-layer stack for gfx950: RMS norm,
+// grouped projections on the f16 matrix cores, and one whole layer (norm,
+// Q/K/V projection, blockwise quantisation, TileMix prefill, output
+// projection with the residual add).
+//
+// Source (web page about TileMix, cited by title and section):
+//   [Explainer] "TileMix：给AI大模型的“注意力”做一次精准的精度分配手术",
+//               section 数字精度混用到底靠不靠谱 (deeper models accumulate more
+//               deviation, the error of a layer being carried into the next).
+//   [Digest]    "TileMix: Tile-Centric Mixed-Precision Attention for LLM
+//               Inference Acceleration", method paragraph (FP16 attention
+//               operands; one static template reused across layers).
+//
+// The pages describe no layer beyond attention.  The stack keeps what carries
+// an error from one layer to the next: attention whose Q, K and V are
+// computed from the running hidden state, and a residual connection.  The
+// hidden state x [T, Hq*d] (fp32) splits into Hkv independent streams of
+// width W = (Hq/Hkv)*d -- stream g is channels g*W .. g*W+W-1, owned by KV
+// head g and its query heads -- and a layer is, per stream,
+//   u = x_g / sqrt(mean(x_g^2) + eps)              (fp16)
+//   [q | k | v] = u . Wqkv_g^T                      (fp16, Wqkv_g (W+2d) x W)
+//   o = TileMix prefill attention of (q, k, v)      (fp16)
+//   x_g += o_g . Wo_g^T                             (fp32, Wo_g W x W)
+// Row n < W of Wqkv_g feeds query head g*Hq/Hkv + n/d, channel n % d; rows
+// W .. W+d-1 feed K of KV head g, the last d rows its V.
+//
+// gfx950 matrix instruction used (lane l of a 64-wide wave, c = l % 32,
+// hh = l / 32): v_mfma_f32_32x32x16_f16 takes A[c][hh*8 + j] and
+// B[hh*8 + j][c], j = 0..7, and leaves accumulator element i (0..15) at
+// C[(i/4)*8 + hh*4 + i%4][c].
+
+#include <hip/hip_runtime.h>
+
+#include "tilemix.h"
+#include "tilemix_host.h"
+#include "tilemix_internal.h"
+
+namespace tilemix {
+namespace stack {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;  // 4 waves of 64
+constexpr int kMaxPerLane = 16;  // W <= 1024 channels per stream
+
+// --------------------------------------------------------------------------
+// RMS norm.  One wave per (token, stream) row of W channels: x viewed as
+// [T*Hkv][W] since Hq*d = Hkv*W.  Sum of squares in fp32, then
+// u = fl16(x * fl32(1 / sqrt(fl32(ss / W) + eps))).
+// --------------------------------------------------------------------------
+struct NormArgs {
+  const float* x;
+  _Float16* u;
+  int64_t rows;  // T * Hkv
+  int32_t W;
+  float eps;
+};
+
+__global__ __launch_bounds__(kThreads) void rms_norm_kernel(NormArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const float* xr = a.x + row * a.W;
+  _Float16* ur = a.u + row * a.W;
+  const int n = a.W >> 6;
+  float v[kMaxPerLane];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    if (i < n) {
+      v[i] = xr[lane + 64 * i];
+      ss = fmaf(v[i], v[i], ss);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float inv = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(ss, (float)a.W) + a.eps));
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i)
+    if (i < n) ur[lane + 64 * i] = (_Float16)(v[i] * inv);
+}
+
+// --------------------------------------------------------------------------
+// Grouped projection C = A_g . B_g^T on the f16 matrix cores, fp32
+// accumulation.  A_g: the stream-g slice of T rows of width W (row stride
+// Hq*d halves); B_g: N rows of W halves (row n = the weights of output n).
+// Workgroup tile 128 tokens x 128 outputs; the W-long reduction runs in
+// 64-wide chunks staged through LDS (rows padded to 144 bytes, so the
+// 16-byte fragment reads of 8 consecutive lanes hit distinct banks); the next
+// chunk's global loads are in flight while the current one is multiplied.
+// Wave (wm, wn) computes the 64 x 64 sub-tile at (64 wm, 64 wn).
+// Epilogue: either Q/K/V in fp16 (kResidual = false) or x += C in fp32.
+// --------------------------------------------------------------------------
+constexpr int kTileM = 128;
+constexpr int kTileN = 128;
+constexpr int kTileK = 64;
+constexpr int kPitch = 144;
+constexpr int kTileBytes = kTileM * kPitch;
+
+struct ProjArgs {
+  const _Float16* a;  // [T, Hq*d]
+  const _Float16* w;  // [Hkv, N, W]
+  _Float16* q;        // [T, Hq, d]
+  _Float16* k;        // [T, Hkv, d]
+  _Float16* v;        // [T, Hkv, d]
+  float* x;           // [T, Hq*d]
+  int64_t T;
+  int32_t W, N, d, hq, hkv;
+};
+
+template <bool kResidual>
+__global__ __launch_bounds__(kThreads, 2) void proj_kernel(ProjArgs p) {
+  __shared__ __attribute__((aligned(16))) char sA[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char sB[kTileBytes];
+  const int g = blockIdx.z;
+  const int64_t m0 = (int64_t)blockIdx.y * kTileM;
+  const int n0 = blockIdx.x * kTileN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int c = lane & 31, hh = lane >> 5;
+  const int64_t lda = (int64_t)p.hq * p.d;
+
+  // Global -> LDS copy: thread tid moves 16 bytes (segment tid % 8) of rows
+  // tid / 8 + 32 j, j = 0..3, of both tiles.  Rows past the end repeat the
+  // last row (their results are not stored).
+  const int lr = tid >> 3, ls = tid & 7;
+  const _Float16* ga[4];
+  const _Float16* gb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = min(m0 + lr + 32 * j, p.T - 1);
+    ga[j] = p.a + t * lda + (int64_t)g * p.W + ls * 8;
+    const int n = min(n0 + lr + 32 * j, p.N - 1);
+    gb[j] = p.w + ((int64_t)g * p.N + n) * p.W + ls * 8;
+  }
+  int4v ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = *reinterpret_cast<const int4v*>(ga[j] + k0);
+      rb[j] = *reinterpret_cast<const int4v*>(gb[j] + k0);
+    }
+  };
+
+  float16v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (float16v){};
+
+  const int nk = p.W / kTileK;
+  gload(0);
+  for (int kc = 0; kc < nk; ++kc) {
+    __syncthreads();  // the previous chunk's fragments have been read
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<int4v*>(sA + (lr + 32 * j) * kPitch + ls * 16) = ra[j];
+      *reinterpret_cast<int4v*>(sB + (lr + 32 * j) * kPitch + ls * 16) = rb[j];
+    }
+    __syncthreads();
+    if (kc + 1 < nk) gload((kc + 1) * kTileK);
+#pragma unroll
+    for (int kk = 0; kk < kTileK / 16; ++kk) {
+      half8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const half8*>(sA + (wm * 64 + i * 32 + c) * kPitch + kk * 32 + hh * 16);
+        bf[i] = *reinterpret_cast<const half8*>(sB + (wn * 64 + i * 32 + c) * kPitch + kk * 32 + hh * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + c;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t t = m0 + wm * 64 + i * 32 + (e / 4) * 8 + hh * 4 + (e % 4);
+        if (t >= p.T) continue;
+        const float val = acc[i][j][e];
+        if (kResidual) {
+          float* px = p.x + t * lda + (int64_t)g * p.W + n;
+          *px = *px + val;
+        } else if (n < p.W) {
+          p.q[t * lda + (int64_t)g * p.W + n] = (_Float16)val;
+        } else if (n < p.W + p.d) {
+          p.k[(t * p.hkv + g) * p.d + (n - p.W)] = (_Float16)val;
+        } else {
+          p.v[(t * p.hkv + g) * p.d + (n - p.W - p.d)] = (_Float16)val;
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Host side
+// --------------------------------------------------------------------------
+namespace {
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TILEMIX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_ptr(const void* p, const char* name, bool needed) {
+  if (!needed) return TILEMIX_OK;
+  if (p == nullptr) return fail(TILEMIX_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(TILEMIX_EINVAL, "%s is not 16-byte aligned", name);
+  return TILEMIX_OK;
+}
+
+int check_shape(int64_t tokens, int32_t hq, int32_t hkv, int32_t d) {
+  if (tokens < 0) return fail(TILEMIX_EINVAL, "tokens = %lld is negative", (long long)tokens);
+  if (d != 64 && d != 128) return fail(TILEMIX_EUNSUPPORTED, "head_dim %d (64 or 128)", d);
+  if (hkv < 1 || hq < 1 || hq % hkv) return fail(TILEMIX_EINVAL, "Hq = %d is not a multiple of Hkv = %d", hq, hkv);
+  if ((int64_t)(hq / hkv) * d > 64 * kMaxPerLane)
+    return fail(TILEMIX_EUNSUPPORTED, "stream width (Hq/Hkv)*d = %d exceeds %d", (hq / hkv) * d, 64 * kMaxPerLane);
+  if (hkv > 65535) return fail(TILEMIX_EINVAL, "Hkv = %d too large for one launch", hkv);
+  if ((tokens + kTileM - 1) / kTileM > 65535) return fail(TILEMIX_EINVAL, "too many tokens for one launch");
+  return TILEMIX_OK;
+}
+
+int launch_norm(const float* x, _Float16* u, int64_t tokens, int32_t hq, int32_t hkv, int32_t d, float eps,
+                hipStream_t st) {
+  NormArgs a;
+  a.x = x;
+  a.u = u;
+  a.rows = tokens * hkv;
+  a.W = (hq / hkv) * d;
+  a.eps = eps;
+  const int64_t blocks = (a.rows + 3) / 4;
+  if (blocks > 0x7fffffff) return fail(TILEMIX_EINVAL, "too many tokens for one launch");
+  hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? TILEMIX_OK : hip_fail(e, "rms norm launch");
+}
+
+int launch_proj(bool residual, const _Float16* a_in, const _Float16* w, _Float16* q, _Float16* k, _Float16* v,
+                float* x, int64_t tokens, int32_t hq, int32_t hkv, int32_t d, hipStream_t st) {
+  ProjArgs p;
+  p.a = a_in;
+  p.w = w;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.x = x;
+  p.T = tokens;
+  p.W = (hq / hkv) * d;
+  p.N = residual ? p.W : p.W + 2 * d;
+  p.d = d;
+  p.hq = hq;
+  p.hkv = hkv;
+  const dim3 grid((p.N + kTileN - 1) / kTileN, (unsigned)((tokens + kTileM - 1) / kTileM), hkv);
+  if (residual)
+    hipLaunchKernelGGL(proj_kernel<true>, grid, dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(proj_kernel<false>, grid, dim3(kThreads), 0, st, p);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? TILEMIX_OK : hip_fail(e, residual ? "output projection launch" : "qkv projection launch");
+}
+
+int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
+
+// Workspace of one layer: the normalised input (reused for the attention
+// output once the projection has read it), Q, K, V, their int8 codes and
+// scales, each at a 256-byte boundary.
+struct LayerWs {
+  int64_t uo, q, k, v, qi, ki, qs, ks, total;
+};
+
+LayerWs layer_ws(const int32_t* plan_h) {
+  const int64_t T = plan_h[kTotalTokens], hq = plan_h[kHq], hkv = plan_h[kHkv], d = plan_h[kHeadDim];
+  LayerWs w;
+  int64_t off = 0;
+  w.uo = off;
+  off += align256(T * hq * d * 2);
+  w.q = off;
+  off += align256(T * hq * d * 2);
+  w.k = off;
+  off += align256(T * hkv * d * 2);
+  w.v = off;
+  off += align256(T * hkv * d * 2);
+  w.qi = off;
+  off += align256(T * hq * d);
+  w.ki = off;
+  off += align256(T * hkv * d);
+  w.qs = off;
+  off += align256(hq * (int64_t)plan_h[kTotalQTiles] * 4);
+  w.ks = off;
+  off += align256(hkv * (int64_t)plan_h[kTotalKTiles] * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+}  // namespace stack
+}  // namespace tilemix
+
+using namespace tilemix;
+using namespace tilemix::stack;
+
+extern "C" {
+
+int tilemix_stack_rms_norm(const float* x, void* u_f16, int64_t tokens, int32_t hq, int32_t hkv,
+                           int32_t head_dim, float eps, void* hip_stream) {
+  clear_error();
+  int rc = check_shape(tokens, hq, hkv, head_dim);
+  if (rc) return rc;
+  if (!(eps >= 0.f)) return fail(TILEMIX_EINVAL, "eps must be >= 0");
+  if ((rc = check_ptr(x, "x", tokens > 0)) || (rc = check_ptr(u_f16, "u_f16", tokens > 0))) return rc;
+  if (tokens == 0) return TILEMIX_OK;
+  return launch_norm(x, static_cast<_Float16*>(u_f16), tokens, hq, hkv, head_dim, eps,
+                     static_cast<hipStream_t>(hip_stream));
+}
+
+int tilemix_stack_qkv(const void* u_f16, const void* wqkv_f16, void* q_f16, void* k_f16, void* v_f16,
+                      int64_t tokens, int32_t hq, int32_t hkv, int32_t head_dim, void* hip_stream) {
+  clear_error();
+  int rc = check_shape(tokens, hq, hkv, head_dim);
+  if (rc) return rc;
+  const bool any = tokens > 0;
+  if ((rc = check_ptr(u_f16, "u_f16", any)) || (rc = check_ptr(wqkv_f16, "wqkv_f16", any)) ||
+      (rc = check_ptr(q_f16, "q_f16", any)) || (rc = check_ptr(k_f16, "k_f16", any)) ||
+      (rc = check_ptr(v_f16, "v_f16", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  return launch_proj(false, static_cast<const _Float16*>(u_f16), static_cast<const _Float16*>(wqkv_f16),
+                     static_cast<_Float16*>(q_f16), static_cast<_Float16*>(k_f16), static_cast<_Float16*>(v_f16),
+                     nullptr, tokens, hq, hkv, head_dim, static_cast<hipStream_t>(hip_stream));
+}
+
+int tilemix_stack_out_residual(const void* o_f16, const void* wo_f16, float* x, int64_t tokens, int32_t hq,
+                               int32_t hkv, int32_t head_dim, void* hip_stream) {
+  clear_error();
+  int rc = check_shape(tokens, hq, hkv, head_dim);
+  if (rc) return rc;
+  const bool any = tokens > 0;
+  if ((rc = check_ptr(o_f16, "o_f16", any)) || (rc = check_ptr(wo_f16, "wo_f16", any)) ||
+      (rc = check_ptr(x, "x", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  return launch_proj(true, static_cast<const _Float16*>(o_f16), static_cast<const _Float16*>(wo_f16), nullptr,
+                     nullptr, nullptr, x, tokens, hq, hkv, head_dim, static_cast<hipStream_t>(hip_stream));
+}
+
+int tilemix_stack_workspace_size(const int32_t* plan_h, int64_t* bytes) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  if (bytes == nullptr) return fail(TILEMIX_EINVAL, "bytes is NULL");
+  *bytes = layer_ws(plan_h).total;
+  return TILEMIX_OK;
+}
+
+int tilemix_stack_layer(const int32_t* plan_h, const int32_t* plan_d, const uint64_t* words_d, float* x,
+                        const void* wqkv_f16, const void* wo_f16, float eps, void* workspace,
+                        int64_t workspace_bytes, void* hip_stream) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const int64_t T = plan_h[kTotalTokens];
+  const int32_t hq = plan_h[kHq], hkv = plan_h[kHkv], d = plan_h[kHeadDim];
+  if ((rc = check_shape(T, hq, hkv, d))) return rc;
+  if (!(eps >= 0.f)) return fail(TILEMIX_EINVAL, "eps must be >= 0");
+  const bool any = T > 0;
+  if ((rc = check_ptr(plan_d, "plan_d", true)) || (rc = check_ptr(words_d, "words_d", any)) ||
+      (rc = check_ptr(x, "x", any)) || (rc = check_ptr(wqkv_f16, "wqkv_f16", any)) ||
+      (rc = check_ptr(wo_f16, "wo_f16", any)) || (rc = check_ptr(workspace, "workspace", any)))
+    return rc;
+  const LayerWs w = layer_ws(plan_h);
+  if (workspace_bytes < w.total)
+    return fail(TILEMIX_EINVAL, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes,
+                (long long)w.total);
+  if (!any) return TILEMIX_OK;
+  char* ws = static_cast<char*>(workspace);
+  _Float16* uo = reinterpret_cast<_Float16*>(ws + w.uo);
+  _Float16* q = reinterpret_cast<_Float16*>(ws + w.q);
+  _Float16* k = reinterpret_cast<_Float16*>(ws + w.k);
+  _Float16* v = reinterpret_cast<_Float16*>(ws + w.v);
+  int8_t* qi = reinterpret_cast<int8_t*>(ws + w.qi);
+  int8_t* ki = reinterpret_cast<int8_t*>(ws + w.ki);
+  float* qs = reinterpret_cast<float*>(ws + w.qs);
+  float* ks = reinterpret_cast<float*>(ws + w.ks);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if ((rc = launch_norm(x, uo, T, hq, hkv, d, eps, st))) return rc;
+  if ((rc = launch_proj(false, uo, static_cast<const _Float16*>(wqkv_f16), q, k, v, nullptr, T, hq, hkv, d, st)))
+    return rc;
+  if ((rc = tilemix_quantize_qk(plan_h, plan_d, q, k, qi, ki, qs, ks, hip_stream))) return rc;
+  if ((rc = tilemix_prefill_varlen(plan_h, plan_d, q, k, v, qi, ki, qs, ks, words_d, uo, hip_stream))) return rc;
+  return launch_proj(true, uo, static_cast<const _Float16*>(wo_f16), nullptr, nullptr, nullptr, x, T, hq, hkv, d,
+                     st);
+}
+
+}  // extern "C"

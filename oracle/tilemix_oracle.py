@@ -917,7 +917,8 @@ def stack_qkv(u, wqkv, hq: int, hkv: int, d: int):
     T = u.shape[0]
     W = stack_width(hq, hkv, d)
     ug = np.asarray(u, dtype=np.float64).reshape(T, hkv, W)
-    y = np.einsum("tgk,gnk->tgn", ug, np.asarray(wqkv, dtype=np.float64)).astype(np.float16)
+    w = np.asarray(wqkv, dtype=np.float64)
+    y = np.stack([ug[:, g, :] @ w[g].T for g in range(hkv)], axis=1).astype(np.float16)
     q = np.ascontiguousarray(y[:, :, :W].reshape(T, hq, d))
     k = np.ascontiguousarray(y[:, :, W:W + d])
     v = np.ascontiguousarray(y[:, :, W + d:])
@@ -931,7 +932,8 @@ def stack_out_residual(x, o16, wo, hq: int, hkv: int, d: int):
     T = x.shape[0]
     W = stack_width(hq, hkv, d)
     og = np.asarray(o16, dtype=np.float64).reshape(T, hkv, W)
-    y = np.einsum("tgk,gnk->tgn", og, np.asarray(wo, dtype=np.float64))
+    w = np.asarray(wo, dtype=np.float64)
+    y = np.stack([og[:, g, :] @ w[g].T for g in range(hkv)], axis=1)
     return x + y.reshape(T, hq * d)
 
 

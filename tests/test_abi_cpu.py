@@ -225,3 +225,48 @@ def test_empty_batch_is_a_no_op():
     # nothing to launch: returns OK without touching device pointers
     assert lib.tilemix_prefill_varlen(p, fake, None, None, None, None, None, None, None, None, None, None) == 0
     assert lib.tilemix_quantize_qk(p, fake, None, None, None, None, None, None, None) == 0
+
+
+# ------------------------------------------------------- multi-layer stack
+
+def test_stack_workspace_size():
+    lens, hq, hkv, d = [300, 0, 77, 129, 1], 6, 2, 64
+    cu = synth.cu_seqlens_of(lens)
+    plan = tm.tilemix_build_plan(cu, hq, hkv, d)
+    T, tq, tk = tm.tilemix_query_sizes(cu)
+
+    def a256(n):
+        return -(-n // 256) * 256
+    want = (2 * a256(T * hq * d * 2) + 2 * a256(T * hkv * d * 2) + a256(T * hq * d) + a256(T * hkv * d)
+            + a256(hq * tq * 4) + a256(hkv * tk * 4))
+    assert tm.tilemix_stack_workspace_size(plan) == want
+
+
+def test_stack_argument_validation():
+    lib = tm.lib()
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: every call below fails validation first
+    # empty input: nothing to do, no pointer needed
+    assert lib.tilemix_stack_rms_norm(None, None, 0, 4, 2, 64, 1e-6, None) == 0
+    assert lib.tilemix_stack_qkv(None, None, None, None, None, 0, 4, 2, 128, None) == 0
+    assert lib.tilemix_stack_out_residual(None, None, None, 0, 4, 2, 64, None) == 0
+    cases = [
+        (lib.tilemix_stack_rms_norm, (fake, fake, 10, 4, 2, 96, 1e-6, None), -2, "head_dim"),
+        (lib.tilemix_stack_rms_norm, (fake, fake, 10, 5, 2, 64, 1e-6, None), -1, "multiple"),
+        (lib.tilemix_stack_rms_norm, (fake, fake, 10, 34, 2, 64, 1e-6, None), -2, "exceeds 1024"),
+        (lib.tilemix_stack_rms_norm, (fake, fake, -1, 4, 2, 64, 1e-6, None), -1, "negative"),
+        (lib.tilemix_stack_rms_norm, (fake, fake, 10, 4, 2, 64, -1.0, None), -1, "eps"),
+        (lib.tilemix_stack_rms_norm, (None, fake, 10, 4, 2, 64, 1e-6, None), -1, "x is NULL"),
+        (lib.tilemix_stack_rms_norm, (fake, P(0x1002), 10, 4, 2, 64, 1e-6, None), -1, "aligned"),
+        (lib.tilemix_stack_qkv, (fake, fake, fake, None, fake, 10, 4, 2, 64, None), -1, "k_f16 is NULL"),
+        (lib.tilemix_stack_out_residual, (fake, None, fake, 10, 4, 2, 64, None), -1, "wo_f16 is NULL"),
+        (lib.tilemix_stack_qkv, (fake, fake, fake, fake, fake, 128 * 65536, 4, 2, 64, None), -1, "tokens"),
+    ]
+    for fn, args, code, text in cases:
+        assert fn(*args) == code, text
+        assert text in tm.tilemix_last_error(), (text, tm.tilemix_last_error())
+    cu = synth.cu_seqlens_of([300, 20])
+    plan = tm.tilemix_build_plan(cu, 4, 2, 64)
+    need = tm.tilemix_stack_workspace_size(plan)
+    rc = lib.tilemix_stack_layer(tm._hptr(plan), fake, fake, fake, fake, fake, 1e-6, fake, need - 1, None)
+    assert rc == -1 and "workspace" in tm.tilemix_last_error()
