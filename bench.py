@@ -23,6 +23,12 @@ three-precision MFMA roofline.
 statistic, the host ranking, and the prefill under the resulting words at the
 same coverage.
 
+``depth`` (skip with --no-depth) runs a synthetic stack of attention +
+residual layers (random weights, one template for every layer) at 0%, 25% and
+the headline coverage side by side: the mean absolute deviation of the hidden
+state from the stack without INT8 groups at every depth, and the time of one
+layer and of each of its kernels against their rooflines.
+
 ``decode`` (skip with --no-decode) times one decode step per sequence against
 an INT8 key/value cache holding the same workload's K and V: tokens/s is new
 tokens per second, and its roofline is HBM bandwidth over the step's
@@ -220,6 +226,118 @@ def bench_fp8(qd, kd, vd, cu, hq, hkv, d, template, mixes, steps):
     return {"template": template, "runs": rows}
 
 
+def bench_depth(cu, hq, hkv, d, template, coverages, n_layers, seed=0, reps=10):
+    """Synthetic stack of attention + residual layers (random weights, one
+    routing template for every layer): the deviation of the hidden state
+    from the stack without INT8 groups at every depth, the time of one layer
+    and of each of its kernels, and their rooflines."""
+    import numpy as np
+    import torch
+    import mixed_precision_attention_amd as tm
+    import synth
+    stream = torch.cuda.current_stream()
+    T = int(cu[-1])
+    C = hq * d
+    W = (hq // hkv) * d
+    wqkv, wo = synth.stack_weights(n_layers, hq, hkv, d, seed=seed)
+    wqkv_d, wo_d = torch.from_numpy(wqkv).cuda(), torch.from_numpy(wo).cuda()
+    x0 = torch.from_numpy(synth.stack_input(T, hq, d, seed=seed + 1)).cuda()
+    covs = [0] + [c for c in coverages if c != 0]
+    stacks = {}
+    for c in covs:
+        st = tm.TileMixStack(cu, hq, hkv, d, template, c)
+        st.set_weights(wqkv_d, wo_d)
+        stacks[c] = st
+    xw = x0.clone()
+    for l in range(2):
+        stacks[covs[-1]].layer(xw, l)
+    del xw
+    xs = {c: x0.clone() for c in covs}
+    ev = {c: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_layers)] for c in covs}
+    dev = {c: [] for c in covs[1:]}
+    mag = []
+    torch.cuda.synchronize()
+    for l in range(n_layers):
+        for c in covs:
+            ev[c][l][0].record(stream)
+            stacks[c].layer(xs[c], l)
+            ev[c][l][1].record(stream)
+        for c in covs[1:]:
+            dev[c].append((xs[c] - xs[0]).abs().mean())
+        mag.append(xs[0].abs().mean())
+    torch.cuda.synchronize()
+    layer_ms = {c: sum(a.elapsed_time(b) for a, b in ev[c]) / n_layers for c in covs}
+    dev = {c: [float(t) for t in v] for c, v in dev.items()}
+    mag = [float(t) for t in mag]
+
+    # one layer's kernels, timed one by one at the last coverage
+    cmain = covs[-1]
+    tp = tm.TileMixPrefill(cu, hq, hkv, d, template, cmain)
+    u = torch.empty((T, C), dtype=torch.float16, device="cuda")
+    q = torch.empty((T, hq, d), dtype=torch.float16, device="cuda")
+    k = torch.empty((T, hkv, d), dtype=torch.float16, device="cuda")
+    v = torch.empty_like(k)
+    o = torch.empty_like(q)
+    xt = x0.clone()
+
+    def timed(fn):
+        fn()
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = {
+        "rms_norm": timed(lambda: tm.tilemix_stack_rms_norm(xt, u, hq, hkv, d, 1e-6)),
+        "qkv_projection": timed(lambda: tm.tilemix_stack_qkv(u, wqkv_d[0], q, k, v, hq, hkv, d)),
+        "quantize": timed(lambda: tp.quantize(q, k)),
+        "prefill": timed(lambda: tp.attend(q, k, v, o)),
+        "out_projection_residual": timed(lambda: tm.tilemix_stack_out_residual(o, wo_d[0], xt, hq, hkv, d)),
+    }
+    # algorithmic bytes and flops of each kernel
+    norm_b = T * C * (4 + 2)
+    qkv_f = 2 * T * W * (W + 2 * d) * hkv
+    qkv_b = T * C * 2 + (T * C + 2 * T * hkv * d) * 2 + hkv * (W + 2 * d) * W * 2
+    out_f = 2 * T * W * W * hkv
+    out_b = T * C * 2 + T * C * 8 + hkv * W * W * 2
+    quant_b = 3 * (T * hq * d + T * hkv * d) + 4 * (hq * tp.tq + hkv * tp.tk)
+    P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
+    attn_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
+    roof = {"rms_norm": norm_b / PEAK_HBM,
+            "qkv_projection": max(qkv_f / PEAK_F16, qkv_b / PEAK_HBM),
+            "quantize": quant_b / PEAK_HBM,
+            "prefill": attn_roof,
+            "out_projection_residual": max(out_f / PEAK_F16, out_b / PEAK_HBM)}
+    kernels = {}
+    for name, f, b in (("rms_norm", 0, norm_b), ("qkv_projection", qkv_f, qkv_b), ("quantize", 0, quant_b),
+                       ("out_projection_residual", out_f, out_b)):
+        t = ms[name] * 1e-3
+        kernels[name] = {"ms": ms[name], "bound": "hbm", "achieved_GBps": b / t / 1e9,
+                         "frac": roof[name] / t, "algorithmic_bytes": b}
+        if f:
+            kernels[name]["tflops"] = f / t / 1e12
+            kernels[name]["flop_bound_frac"] = f / PEAK_F16 / t
+    kernels["prefill"] = {"ms": ms["prefill"], "bound": "mfma", "frac": attn_roof / (ms["prefill"] * 1e-3)}
+    t_roof = sum(roof.values())
+    depths = [1, 2, 4, 8, 12, 16, 24, 32]
+    return {
+        "workload": f"synthetic stack, {n_layers} layers of attention + residual, streams of width {W}",
+        "template": template, "layers": n_layers,
+        "deviation": {str(c): [round(x, 7) for x in v] for c, v in dev.items()},
+        "hidden_mean_abs": [round(x, 5) for x in mag],
+        "deviation_at": {str(c): {str(l): v[l - 1] for l in depths if l <= n_layers} for c, v in dev.items()},
+        "layer_ms": {str(c): t for c, t in layer_ms.items()},
+        "layer_roofline_us": t_roof * 1e6,
+        "layer_frac": t_roof / (layer_ms[cmain] * 1e-3),
+        "kernels": kernels,
+    }
+
+
 def decode_bytes(cu, hq, hkv, d, tq, tk):
     """Algorithmic HBM bytes of one decode step: the INT8 cache (K and V) and
     its scales read once, the routing words, the queries read and the output
@@ -383,6 +501,9 @@ def main(argv=None):
                     help="skip the three-path (FP16/FP8/INT8) prefill leg")
     ap.add_argument("--no-adaptive", action="store_true",
                     help="skip the adaptive-routing leg (importance statistic + prefill under its words)")
+    ap.add_argument("--no-depth", action="store_true",
+                    help="skip the synthetic multi-layer stack (deviation by depth)")
+    ap.add_argument("--depth-layers", type=int, default=32)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
@@ -507,6 +628,8 @@ def main(argv=None):
         result["fp8"] = bench_fp8(qd, kd, vd, cu, hq, hkv, d, template, [(5000, 2500), (0, 7500)], 20)
     if not args.no_adaptive:
         result["adaptive"] = bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, 20)
+    if not args.no_depth:
+        result["depth"] = bench_depth(cu, hq, hkv, d, template, [2500, coverage], args.depth_layers)
     if not args.no_decode:
         spec_named = dict(spec, name=args.workload)
         result["decode"] = bench_decode(q, k, v, cu, spec_named, template, coverage, args.decode_steps,
