@@ -47,7 +47,8 @@ constexpr int kMaxPerLane = 16;  // W <= 1024 channels per stream
 
 // --------------------------------------------------------------------------
 // RMS norm.  One wave per (token, stream) row of W channels: x viewed as
-// [T*Hkv][W] since Hq*d = Hkv*W.  Sum of squares in fp32, then
+// [T*Hkv][W] since Hq*d = Hkv*W; each lane holds kVec-wide pieces (kVec = 4,
+// 2 or 1 as W allows) in registers.  Sum of squares in fp32, then
 // u = fl16(x * fl32(1 / sqrt(fl32(ss / W) + eps))).
 // --------------------------------------------------------------------------
 struct NormArgs {
@@ -58,28 +59,38 @@ struct NormArgs {
   float eps;
 };
 
+template <int kVec>
 __global__ __launch_bounds__(kThreads) void rms_norm_kernel(NormArgs a) {
+  typedef float floatv __attribute__((ext_vector_type(kVec)));
+  typedef _Float16 halfv __attribute__((ext_vector_type(kVec)));
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= a.rows) return;
-  const float* xr = a.x + row * a.W;
-  _Float16* ur = a.u + row * a.W;
-  const int n = a.W >> 6;
-  float v[kMaxPerLane];
+  const floatv* xr = reinterpret_cast<const floatv*>(a.x + row * a.W);
+  halfv* ur = reinterpret_cast<halfv*>(a.u + row * a.W);
+  const int n = a.W / (64 * kVec);
+  floatv v[kMaxPerLane / kVec];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < kMaxPerLane / kVec; ++i) {
     if (i < n) {
       v[i] = xr[lane + 64 * i];
-      ss = fmaf(v[i], v[i], ss);
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) ss = fmaf(v[i][j], v[i][j], ss);
     }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   const float inv = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(ss, (float)a.W) + a.eps));
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i)
-    if (i < n) ur[lane + 64 * i] = (_Float16)(v[i] * inv);
+  for (int i = 0; i < kMaxPerLane / kVec; ++i) {
+    if (i < n) {
+      halfv h;
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) h[j] = (_Float16)(v[i][j] * inv);
+      ur[lane + 64 * i] = h;
+    }
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -108,15 +119,26 @@ struct ProjArgs {
   float* x;           // [T, Hq*d]
   int64_t T;
   int32_t W, N, d, hq, hkv;
+  int32_t col_tiles, row_tiles, units;  // units = Hkv * row_tiles * col_tiles
 };
 
+constexpr int kDies = 8;  // XCDs of an MI355X; workgroups are dealt round-robin
+
 template <bool kResidual>
-__global__ __launch_bounds__(kThreads, 2) void proj_kernel(ProjArgs p) {
-  __shared__ __attribute__((aligned(16))) char sA[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char sB[kTileBytes];
-  const int g = blockIdx.z;
-  const int64_t m0 = (int64_t)blockIdx.y * kTileM;
-  const int n0 = blockIdx.x * kTileN;
+__global__ __launch_bounds__(kThreads, 4) void proj_kernel(ProjArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
+  char* sA = smem;
+  char* sB = smem + kTileBytes;
+  // XCD-aware order: workgroup i runs on die i % 8, so unit
+  // u = (i % 8) * per_die + i / 8 gives each die a contiguous run of units,
+  // column tiles fastest: the column tiles that share a token tile's A rows
+  // meet in one die's L2, and a die works through few streams' weights.
+  const int64_t per_die = ((int64_t)p.units + kDies - 1) / kDies;
+  const int64_t u = (int64_t)(blockIdx.x % kDies) * per_die + blockIdx.x / kDies;
+  if (u >= p.units) return;  // before any barrier
+  const int n0 = (int)(u % p.col_tiles) * kTileN;
+  const int64_t m0 = ((u / p.col_tiles) % p.row_tiles) * kTileM;
+  const int g = (int)(u / ((int64_t)p.col_tiles * p.row_tiles));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int c = lane & 31, hh = lane >> 5;
@@ -125,22 +147,26 @@ __global__ __launch_bounds__(kThreads, 2) void proj_kernel(ProjArgs p) {
   // Global -> LDS copy: thread tid moves 16 bytes (segment tid % 8) of rows
   // tid / 8 + 32 j, j = 0..3, of both tiles.  Rows past the end repeat the
   // last row (their results are not stored).
+  // Addresses: a wave-uniform base per tile plus 32-bit lane offsets (the
+  // tile spans at most 128 rows), which keeps the copy's address registers
+  // few enough for four workgroups per CU.
   const int lr = tid >> 3, ls = tid & 7;
-  const _Float16* ga[4];
-  const _Float16* gb[4];
+  const _Float16* abase = p.a + m0 * lda + (int64_t)g * p.W;
+  const _Float16* bbase = p.w + ((int64_t)g * p.N + n0) * p.W;
+  uint32_t oa[4], ob[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t t = min(m0 + lr + 32 * j, p.T - 1);
-    ga[j] = p.a + t * lda + (int64_t)g * p.W + ls * 8;
-    const int n = min(n0 + lr + 32 * j, p.N - 1);
-    gb[j] = p.w + ((int64_t)g * p.N + n) * p.W + ls * 8;
+    const int64_t t = min(m0 + lr + 32 * j, p.T - 1) - m0;
+    oa[j] = (uint32_t)(t * lda) + ls * 8;
+    const int n = min(n0 + lr + 32 * j, p.N - 1) - n0;
+    ob[j] = (uint32_t)(n * p.W) + ls * 8;
   }
   int4v ra[4], rb[4];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ra[j] = *reinterpret_cast<const int4v*>(ga[j] + k0);
-      rb[j] = *reinterpret_cast<const int4v*>(gb[j] + k0);
+      ra[j] = *reinterpret_cast<const int4v*>(abase + oa[j] + k0);
+      rb[j] = *reinterpret_cast<const int4v*>(bbase + ob[j] + k0);
     }
   };
 
@@ -177,29 +203,82 @@ __global__ __launch_bounds__(kThreads, 2) void proj_kernel(ProjArgs p) {
     }
   }
 
+  // Epilogue.  Each wave's 64 x 64 block goes out in two halves of 32 rows:
+  // the accumulators are written to a wave-private LDS area (rows of 72
+  // floats, so the two half-waves, 4 rows apart, hit disjoint banks), then
+  // read back as 16-byte row pieces and stored (fp16 Q/K/V) or added to x
+  // (fp32) with full vectors, all of a lane's loads in flight together.
+  // N, W and d are multiples of 64, so a wave's 64 columns lie in one of
+  // q, k, v and either all or none of them exist.
+  __syncthreads();  // every wave is done with the operand tiles
+  const int nb = n0 + wn * 64;
+  if (nb >= p.N) return;  // no barrier follows
+  constexpr int kRow = 72;
+  float* sC = reinterpret_cast<float*>(smem) + wave * (32 * kRow);
+  int64_t stride;
+  char* dst;
+  if (kResidual) {
+    stride = lda * 4;
+    dst = reinterpret_cast<char*>(p.x + (int64_t)g * p.W + nb);
+  } else if (nb < p.W) {
+    stride = lda * 2;
+    dst = reinterpret_cast<char*>(p.q + (int64_t)g * p.W + nb);
+  } else if (nb < p.W + p.d) {
+    stride = (int64_t)p.hkv * p.d * 2;
+    dst = reinterpret_cast<char*>(p.k + (int64_t)g * p.d + (nb - p.W));
+  } else {
+    stride = (int64_t)p.hkv * p.d * 2;
+    dst = reinterpret_cast<char*>(p.v + (int64_t)g * p.d + (nb - p.W - p.d));
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + c;
-      if (n >= p.N) continue;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t t = m0 + wm * 64 + i * 32 + (e / 4) * 8 + hh * 4 + (e % 4);
-        if (t >= p.T) continue;
-        const float val = acc[i][j][e];
-        if (kResidual) {
-          float* px = p.x + t * lda + (int64_t)g * p.W + n;
-          *px = *px + val;
-        } else if (n < p.W) {
-          p.q[t * lda + (int64_t)g * p.W + n] = (_Float16)val;
-        } else if (n < p.W + p.d) {
-          p.k[(t * p.hkv + g) * p.d + (n - p.W)] = (_Float16)val;
-        } else {
-          p.v[(t * p.hkv + g) * p.d + (n - p.W - p.d)] = (_Float16)val;
+      for (int e = 0; e < 16; ++e) sC[((e >> 2) * 8 + hh * 4 + (e & 3)) * kRow + j * 32 + c] = acc[i][j][e];
+    __builtin_amdgcn_wave_barrier();
+    const int64_t r0 = m0 + wm * 64 + i * 32;
+    // 32 rows x 16 float4: lane handles piece lane + 64 s -> row 4 s + lane / 16,
+    // column 4 (lane % 16); four pieces per batch
+    const int col4 = (lane & 15) * 4;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float4 part[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int row = 4 * (4 * b + s4) + (lane >> 4);
+        part[s4] = *reinterpret_cast<const float4*>(sC + row * kRow + col4);
+      }
+      if (kResidual) {
+        float4 xv[4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int64_t t = r0 + 4 * (4 * b + s4) + (lane >> 4);
+          if (t < p.T) xv[s4] = *reinterpret_cast<const float4*>(dst + t * stride + col4 * 4);
+        }
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int64_t t = r0 + 4 * (4 * b + s4) + (lane >> 4);
+          if (t < p.T) {
+            const float4 o = {xv[s4].x + part[s4].x, xv[s4].y + part[s4].y, xv[s4].z + part[s4].z,
+                              xv[s4].w + part[s4].w};
+            *reinterpret_cast<float4*>(dst + t * stride + col4 * 4) = o;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int64_t t = r0 + 4 * (4 * b + s4) + (lane >> 4);
+          if (t < p.T) {
+            typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+            const half4v h = {(_Float16)part[s4].x, (_Float16)part[s4].y, (_Float16)part[s4].z,
+                              (_Float16)part[s4].w};
+            *reinterpret_cast<half4v*>(dst + t * stride + col4 * 2) = h;
+          }
         }
       }
     }
+    __builtin_amdgcn_wave_barrier();  // the second half reuses the area
   }
 }
 
@@ -240,7 +319,12 @@ int launch_norm(const float* x, _Float16* u, int64_t tokens, int32_t hq, int32_t
   a.eps = eps;
   const int64_t blocks = (a.rows + 3) / 4;
   if (blocks > 0x7fffffff) return fail(TILEMIX_EINVAL, "too many tokens for one launch");
-  hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  if (a.W % 256 == 0)
+    hipLaunchKernelGGL(rms_norm_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else if (a.W % 128 == 0)
+    hipLaunchKernelGGL(rms_norm_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(rms_norm_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? TILEMIX_OK : hip_fail(e, "rms norm launch");
 }
@@ -260,7 +344,12 @@ int launch_proj(bool residual, const _Float16* a_in, const _Float16* w, _Float16
   p.d = d;
   p.hq = hq;
   p.hkv = hkv;
-  const dim3 grid((p.N + kTileN - 1) / kTileN, (unsigned)((tokens + kTileM - 1) / kTileM), hkv);
+  p.col_tiles = (p.N + kTileN - 1) / kTileN;
+  p.row_tiles = (int32_t)((tokens + kTileM - 1) / kTileM);
+  const int64_t units = (int64_t)hkv * p.row_tiles * p.col_tiles;
+  if (units > 0x7fffffff - kDies) return fail(TILEMIX_EINVAL, "too many tokens for one launch");
+  p.units = (int32_t)units;
+  const dim3 grid((unsigned)((units + kDies - 1) / kDies * kDies));
   if (residual)
     hipLaunchKernelGGL(proj_kernel<true>, grid, dim3(kThreads), 0, st, p);
   else
