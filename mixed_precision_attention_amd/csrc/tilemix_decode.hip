@@ -156,7 +156,10 @@ __device__ inline void i8x4_to_half(uint32_t w, half2v& lo, half2v& hi) {
   hi = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) - bias;
 }
 
-template <int D>
+// kG: query heads of the workgroup known at compile time when a KV head has
+// fewer than kMaxG of them (kG = kMaxG: a runtime count, the last group of a
+// larger set may be partial).
+template <int D, int kG>
 __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs a) {
   __shared__ Smem<D> sm;
   const int chunk = blockIdx.x;
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs 
   if (chunk * kChunk >= L) return;  // no keys here (the merge reads only live chunks)
   const int grp = a.hq / a.hkv;
   const int h0 = kv * grp + hg * kMaxG;
-  const int G = min(kMaxG, grp - hg * kMaxG);
+  const int G = kG < kMaxG ? kG : min(kMaxG, grp - hg * kMaxG);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
 
@@ -240,10 +243,10 @@ __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs 
   __syncthreads();
 
   // Scores of this wave's key tile, one key per lane, in the log2 domain.
-  float xs[kMaxG];
+  float xs[kG];
   if (bit) {
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
+    for (int h = 0; h < kG; ++h) {
       if (h >= G) break;
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(sm.qi[h]);
       int acc = 0;
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs 
     for (int i = 0; i < D / 4; ++i) i8x4_to_half(kw[i], kh[2 * i], kh[2 * i + 1]);
     const float f = s_k * inv_sqrt_d * kLog2e;
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
+    for (int h = 0; h < kG; ++h) {
       if (h >= G) break;
       const half2v* qh = reinterpret_cast<const half2v*>(sm.qf[h]);
       float acc = 0.f;
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs 
 
   // Chunk softmax state per head (log2 domain, relative to the chunk max).
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  for (int h = 0; h < kG; ++h) {
     if (h >= G) break;
     float m = live ? xs[h] : -INFINITY;
 #pragma unroll
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs 
   }
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  for (int h = 0; h < kG; ++h) {
     if (h >= G) break;
     const float m = fmaxf(fmaxf(sm.mx[0][h], sm.mx[1][h]), fmaxf(sm.mx[2][h], sm.mx[3][h]));
     // P rounded to fp16; the normaliser sums the same rounded values
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs 
   // with fp16 pair dot products (fp16 P and int8 values are exact in fp16;
   // products exact, fp32 sums), then applies its key tile's value scale (a
   // part lies inside one key tile).
-  float acc[kMaxG][4] = {};
+  float acc[kG][4] = {};
 #pragma unroll
   for (int k = 0; k < kKeys; k += 2) {
     const int key = part * kKeys + k;
@@ -306,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs 
     i8x4_to_half(__builtin_amdgcn_perm(vreg[k + 1], vreg[k], 0x05010400u), v01[0], v01[1]);
     i8x4_to_half(__builtin_amdgcn_perm(vreg[k + 1], vreg[k], 0x07030602u), v01[2], v01[3]);
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
+    for (int h = 0; h < kG; ++h) {
       if (h >= G) break;
       const half2v pp = *reinterpret_cast<const half2v*>(&sm.pv[h][key]);
 #pragma unroll
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs 
   // Sum the parts: lanes l, l + kGroups, ... of a wave hold the same
   // channels, then the four waves through LDS.
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  for (int h = 0; h < kG; ++h) {
     if (h >= G) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -401,6 +404,20 @@ int check_ptr(const void* p, const char* name, bool needed) {
   if (p == nullptr) return fail(TILEMIX_EINVAL, "%s is NULL", name);
   if (!aligned16(p)) return fail(TILEMIX_EINVAL, "%s is not 16-byte aligned", name);
   return TILEMIX_OK;
+}
+
+template <int D>
+void launch_partial(int kg, dim3 grid, hipStream_t st, const DecodeArgs& a) {
+  switch (kg) {
+    case 1: hipLaunchKernelGGL((decode_partial_kernel<D, 1>), grid, dim3(kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_partial_kernel<D, 2>), grid, dim3(kThreads), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((decode_partial_kernel<D, 3>), grid, dim3(kThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((decode_partial_kernel<D, 4>), grid, dim3(kThreads), 0, st, a); break;
+    case 5: hipLaunchKernelGGL((decode_partial_kernel<D, 5>), grid, dim3(kThreads), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((decode_partial_kernel<D, 6>), grid, dim3(kThreads), 0, st, a); break;
+    case 7: hipLaunchKernelGGL((decode_partial_kernel<D, 7>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((decode_partial_kernel<D, kMaxG>), grid, dim3(kThreads), 0, st, a); break;
+  }
 }
 
 // Chunks of the longest sequence.
@@ -507,10 +524,10 @@ int tilemix_decode_varlen(const int32_t* plan_h, const int32_t* plan_d, const vo
   if (gy > 65535 || a.chunks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
   const int d = plan_h[kHeadDim];
   if (a.chunks > 0) {
-    if (d == 64)
-      hipLaunchKernelGGL(decode_partial_kernel<64>, dim3(a.chunks, (unsigned)gy), dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL(decode_partial_kernel<128>, dim3(a.chunks, (unsigned)gy), dim3(kThreads), 0, st, a);
+    const dim3 grid(a.chunks, (unsigned)gy);
+    const int kg = std::min(grp, kMaxG);
+    if (d == 64) launch_partial<64>(kg, grid, st, a);
+    else launch_partial<128>(kg, grid, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
