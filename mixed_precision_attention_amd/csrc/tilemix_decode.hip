@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
   float acc[D / 64] = {};
-#pragma unroll 4
+#pragma unroll 16
   for (int i = 0; i < n; ++i) {
     const float* r = base + (size_t)i * (D + 2);
     const float wgt = __builtin_amdgcn_exp2f(r[0] - M);
