@@ -23,6 +23,13 @@ three-precision MFMA roofline.
 statistic, the host ranking, and the prefill under the resulting words at the
 same coverage.
 
+``sweep_headline`` and ``sweep`` (skip with --no-sweep) time the fused
+prefill at INT8 coverages 0, 10, 25, 50, 75 and 100% -- the headline
+workload's template, then every template at L=8192 -- with tokens/s, the
+roofline fraction, whether tokens/s is non-decreasing in coverage, and
+MAD(c), the mean absolute difference of all fp16 outputs from the same
+kernel at 0%.
+
 ``depth`` (skip with --no-depth) runs a synthetic stack of attention +
 residual layers (random weights, one template for every layer) at 0%, 25% and
 the headline coverage side by side: the mean absolute deviation of the hidden
@@ -338,6 +345,58 @@ def bench_depth(cu, hq, hkv, d, template, coverages, n_layers, seed=0, reps=10):
     }
 
 
+SWEEP_TEMPLATES = ("band", "global", "rowrandom", "alignedsparse", "bigbird", "sptrans")
+SWEEP_COVERAGES = (0, 1000, 2500, 5000, 7500, 10000)
+
+
+def bench_sweep(workload, templates, coverages, steps=20):
+    """Coverage sweep of the fused prefill over every template on one
+    workload: kernel time, tokens/s, its monotonicity in coverage, and
+    MAD(c) = mean |O_c - O_0%| over all fp16 outputs against the same kernel
+    without INT8 groups (the analogue of the pages' deviation-by-coverage
+    measurement)."""
+    import torch
+    import mixed_precision_attention_amd as tm
+    import synth
+    q, k, v, cu, spec = synth.make_workload(workload)
+    hq, hkv, d = spec["hq"], spec["hkv"], spec["d"]
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    del q, k, v
+    stream = torch.cuda.current_stream()
+    tp = tm.TileMixPrefill(cu, hq, hkv, d, templates[0], 0)
+    tp.quantize(qd, kd)
+    o_ref = torch.empty_like(qd)
+    tp.attend(qd, kd, vd, o_ref)  # 0%: no INT8 group, the same for every template
+    out = torch.empty_like(qd)
+    tokens = int(cu[-1])
+    res = {}
+    for template in templates:
+        rows = []
+        for cov in coverages:
+            tp.set_routing(template, cov)
+            for _ in range(3):
+                tp.attend(qd, kd, vd, out)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                tp.attend(qd, kd, vd, out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            mad = float((out.float() - o_ref.float()).abs().mean())
+            P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
+            t_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
+            rows.append({"coverage_bp": cov, "prefill_ms": round(ms, 4), "tokens_per_s": tokens / (ms * 1e-3),
+                         "frac": round(t_roof / (ms * 1e-3), 4), "int8_pair_share": round(P8 / P, 4),
+                         "mad_vs_0": mad})
+        tps = [r["tokens_per_s"] for r in rows]
+        res[template] = {"runs": rows,
+                         "monotone": all(b >= a for a, b in zip(tps, tps[1:])),
+                         "monotone_within_1pct": all(b >= 0.99 * a for a, b in zip(tps, tps[1:])),
+                         "mad_monotone": all(b["mad_vs_0"] >= a["mad_vs_0"] for a, b in zip(rows, rows[1:]))}
+    return {"workload": workload, "steps": steps, "templates": res}
+
+
 def decode_bytes(cu, hq, hkv, d, tq, tk):
     """Algorithmic HBM bytes of one decode step: the INT8 cache (K and V) and
     its scales read once, the routing words, the queries read and the output
@@ -501,6 +560,9 @@ def main(argv=None):
                     help="skip the three-path (FP16/FP8/INT8) prefill leg")
     ap.add_argument("--no-adaptive", action="store_true",
                     help="skip the adaptive-routing leg (importance statistic + prefill under its words)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the coverage sweep over every template at L=8192 (time and MAD by coverage)")
+    ap.add_argument("--sweep-workload", default="llama3b_l8k")
     ap.add_argument("--no-depth", action="store_true",
                     help="skip the synthetic multi-layer stack (deviation by depth)")
     ap.add_argument("--depth-layers", type=int, default=32)
@@ -628,6 +690,10 @@ def main(argv=None):
         result["fp8"] = bench_fp8(qd, kd, vd, cu, hq, hkv, d, template, [(5000, 2500), (0, 7500)], 20)
     if not args.no_adaptive:
         result["adaptive"] = bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, 20)
+    if not args.no_sweep:
+        # the headline workload's SpTrans sweep, then every template at L=8192
+        result["sweep_headline"] = bench_sweep(args.workload, (template,), SWEEP_COVERAGES)
+        result["sweep"] = bench_sweep(args.sweep_workload, SWEEP_TEMPLATES, SWEEP_COVERAGES)
     if not args.no_depth:
         result["depth"] = bench_depth(cu, hq, hkv, d, template, [2500, coverage], args.depth_layers)
     if not args.no_decode:
