@@ -245,3 +245,21 @@ def test_deviation_grows_with_coverage():
     base = run_gpu(q, k, v, cu, hq, hkv, "band", 0)["out"].astype(np.float64)
     mads = [np.mean(np.abs(run_gpu(q, k, v, cu, hq, hkv, "band", c)["out"] - base)) for c in (2500, 5000, 10000)]
     assert 0 < mads[0] <= mads[1] <= mads[2]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_lossless_inputs_coverage_independent(d):
+    # Q blocks (128 rows) and K blocks (64 rows) of values k * 2^-6 with one
+    # +-127 * 2^-6 per (block, head): the scale is 2^-6 and the codes are k,
+    # so both score paths give the same exact scores (products and partial
+    # sums exact in fp32, the scale factors differ by powers of two) and the
+    # output does not depend on the routing at all.
+    lens, hq, hkv = [300, 77, 129, 1], 4, 2
+    _log(f"lossless inputs d={d}")
+    q = synth.lossless_blocks(lens, hq, d, 128, seed=27)
+    k = synth.lossless_blocks(lens, hkv, d, 64, seed=28)
+    _, _, v, cu = synth.make_qkv(lens, hq, hkv, d, False, 29)
+    base = run_gpu(q, k, v, cu, hq, hkv, "band", 0)["out"]
+    for template, cov in (("band", 5000), ("rowrandom", 2500), ("sptrans", 10000)):
+        assert np.array_equal(run_gpu(q, k, v, cu, hq, hkv, template, cov)["out"], base), (template, cov)
+    assert_close(base, naive_causal_attention(q, k, v, cu, hq, hkv))
