@@ -30,6 +30,8 @@
 namespace tilemix {
 namespace adaptive {
 
+typedef int int4v __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kMaxRowTiles = 4096;  // key tiles of one row held in LDS
 
@@ -54,10 +56,11 @@ __device__ inline int seq_of_tile(const int32_t* seqtab, int batch, int field, i
   return lo;
 }
 
-// Column sums of one (block, head): thread (4 columns, row part).
+// Column sums of one (block, head): thread (16 columns, row part), 16-byte
+// loads.
 template <int D>
 __global__ __launch_bounds__(kThreads) void block_colsum_kernel(ImpArgs a) {
-  constexpr int kGroups = D / 4, kParts = kThreads / kGroups;
+  constexpr int kGroups = D / 16, kParts = kThreads / kGroups;
   __shared__ int part[kParts][D];
   const int32_t* seqtab = a.plan + kHeaderLen;
   int bid = blockIdx.x;
@@ -71,15 +74,15 @@ __global__ __launch_bounds__(kThreads) void block_colsum_kernel(ImpArgs a) {
   const int row0 = rec[kSeqStart] + local * blk;
   const int nrows = min(blk, rec[kSeqLen] - local * blk);
   const int8_t* src = (is_k ? a.ki8 : a.qi8) + ((size_t)row0 * H + head) * D;
-  const int tid = threadIdx.x, c4 = tid % kGroups, p = tid / kGroups;
-  int acc[4] = {0, 0, 0, 0};
+  const int tid = threadIdx.x, c16 = tid % kGroups, p = tid / kGroups;
+  int acc[16] = {};
   for (int r = p; r < nrows; r += kParts) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (size_t)r * H * D + c4 * 4);
+    const int4v w = *reinterpret_cast<const int4v*>(src + (size_t)r * H * D + c16 * 16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += (int)(int8_t)((w >> (8 * e)) & 0xff);
+    for (int e = 0; e < 16; ++e) acc[e] += (int)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xff);
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) part[p][c4 * 4 + e] = acc[e];
+  for (int e = 0; e < 16; ++e) part[p][c16 * 16 + e] = acc[e];
   __syncthreads();
   if (tid < D) {
     int sum = 0;
@@ -90,12 +93,15 @@ __global__ __launch_bounds__(kThreads) void block_colsum_kernel(ImpArgs a) {
   }
 }
 
-// Importance of every group of one (KV head, query-tile row).
+// Importance of every group of one (KV head, query-tile row).  One thread
+// per (key tile, query head): the column-sum dot product in float64, exact
+// here (integer products below 2^27, sums below 2^35), so (float)dot is the
+// binary32 rounding of the exact integer.
 template <int D>
 __global__ __launch_bounds__(kThreads) void importance_kernel(ImpArgs a) {
   __shared__ float zt[kMaxRowTiles];
   __shared__ float red[kThreads / 64];
-  extern __shared__ int32_t qsum_l[];  // [grp][D]
+  extern __shared__ double qsum_l[];  // [grp][D]
   const int32_t* seqtab = a.plan + kHeaderLen;
   const int kv = blockIdx.x / a.tq, tile = blockIdx.x % a.tq;
   const int s = seq_of_tile(seqtab, a.batch, kSeqQtOff, tile);
@@ -106,26 +112,44 @@ __global__ __launch_bounds__(kThreads) void importance_kernel(ImpArgs a) {
   const int nq = min(kBlockM, L - kBlockM * r);
   const int tid = threadIdx.x;
   for (int i = tid; i < grp * D; i += kThreads)
-    qsum_l[i] = a.qsum[((size_t)(h0 + i / D) * a.tq + tile) * D + i % D];
+    qsum_l[i] = (double)a.qsum[((size_t)(h0 + i / D) * a.tq + tile) * D + i % D];
+  for (int t = tid; t < nt; t += kThreads) zt[t] = -INFINITY;
   __syncthreads();
-  float rowmax = -INFINITY;
-  for (int t = tid; t < nt; t += kThreads) {
+  // Z(t) = max over the query heads of fl32(dot) * fl32(fl32(s_q s_k) / (n_q n_k))
+  for (int item = tid; item < nt * grp; item += kThreads) {
+    const int t = item / grp, h = item % grp;
     const int kt = kt0 + t;
     const int nk = min(kBlockN, L - kBlockN * t);
-    const int32_t* ksr = a.ksum + ((size_t)kv * a.tk + kt) * D;
-    const float sk = a.ks[(size_t)kv * a.tk + kt];
-    float Z = -INFINITY;
-    for (int h = 0; h < grp; ++h) {
-      long long dot = 0;
+    const int4v* ksr = reinterpret_cast<const int4v*>(a.ksum + ((size_t)kv * a.tk + kt) * D);
+    const double* qh = qsum_l + h * D;
+    // four independent exact partial sums (every partial sum is an integer
+    // well inside float64's exact range, so the order does not matter)
+    double d4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 8
-      for (int c = 0; c < D; ++c) dot += (long long)qsum_l[h * D + c] * (long long)ksr[c];
-      const float aa = __fmul_rn(a.qs[(size_t)(h0 + h) * a.tq + tile], sk);
-      const float b = __fdiv_rn(aa, (float)(nq * nk));
-      Z = fmaxf(Z, __fmul_rn((float)dot, b));
+    for (int c4 = 0; c4 < D / 4; ++c4) {
+      const int4v kk = ksr[c4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d4[e] = __builtin_fma(qh[4 * c4 + e], (double)kk[e], d4[e]);
     }
-    zt[t] = Z;
-    rowmax = fmaxf(rowmax, Z);
+    const double dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+    const float sk = a.ks[(size_t)kv * a.tk + kt];
+    const float aa = __fmul_rn(a.qs[(size_t)(h0 + h) * a.tq + tile], sk);
+    const float b = __fdiv_rn(aa, (float)(nq * nk));
+    // the max over heads is order-independent: combine them in LDS (each
+    // failed exchange means another head raised the slot, so at most grp
+    // rounds)
+    const float z = __fmul_rn((float)dot, b);
+    float* slot = &zt[t];
+    float old = *slot;
+    while (z > old) {
+      const unsigned prev = atomicCAS(reinterpret_cast<unsigned*>(slot), __float_as_uint(old), __float_as_uint(z));
+      if (prev == __float_as_uint(old)) break;
+      old = __uint_as_float(prev);
+    }
   }
+  __syncthreads();
+  float rowmax = -INFINITY;
+  for (int t = tid; t < nt; t += kThreads) rowmax = fmaxf(rowmax, zt[t]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) rowmax = fmaxf(rowmax, __shfl_xor(rowmax, off));
   if ((tid & 63) == 0) red[tid >> 6] = rowmax;
@@ -211,7 +235,7 @@ int tilemix_routing_importance(const int32_t* plan_h, const int32_t* plan_d, con
   const int d = plan_h[kHeadDim];
   const int64_t b1 = (int64_t)a.tq * a.hq + (int64_t)a.tk * a.hkv, b2 = (int64_t)a.hkv * a.tq;
   if (b1 > 0x7fffffff || b2 > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
-  const size_t lds = (size_t)(a.hq / a.hkv) * d * sizeof(int32_t);
+  const size_t lds = (size_t)(a.hq / a.hkv) * d * sizeof(double);
   if (lds > 64 * 1024) return fail(TILEMIX_EUNSUPPORTED, "too many query heads per KV head");
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (d == 64) {
