@@ -1,15 +1,20 @@
 /*
- * tilemix.h -- C ABI of the MI355X (gfx950) TileMix prefill library.
+ * tilemix.h -- C ABI of the MI355X (gfx950) TileMix library.
  *
  * TileMix is causal dense prefill attention in one fused streaming kernel in
  * which every hardware-aligned score-tile group computes Q.K^T either in FP16
- * or in blockwise INT8, and all groups share one online-softmax state.
+ * or in blockwise INT8, and all groups share one online-softmax state.  Besides
+ * that path the library offers one decode step against an INT8 key/value
+ * cache, content-dependent routing words, an FP8 (E4M3) third score path and
+ * the layers of a synthetic attention stack that carries the deviation from
+ * layer to layer.
  *
  * Sources (web pages about TileMix), cited by title and section:
  *   [Digest]    "TileMix: Tile-Centric Mixed-Precision Attention for LLM
  *               Inference Acceleration" (paper digest), method and setup.
  *   [Explainer] "TileMix：给AI大模型的“注意力”做一次精准的精度分配手术"
- *               (popular explainer), sections 第一步 / 第二步 / 第三步 / 支持的场景.
+ *               (popular explainer), sections 第一步 / 第二步 / 第三步 / 支持的场景 /
+ *               数字精度混用到底靠不靠谱 / 写在后面.
  *   [Routes]    "TileMix Routes Attention Precision at the Hardware-Tile
  *               Level", section "Precision routing over score tiles".
  *   [Map]       "Precision Has a Map: TileMix Routes INT8 Inside Dense
@@ -201,8 +206,11 @@ int tilemix_quantize_qk_fp8(const int32_t* plan_h, const int32_t* plan_d, const 
 
 /* Three-path fused prefill (device): as tilemix_prefill_varlen, and a group
  * whose bit is set in words_f8_d (and not in words_i8_d) computes
- * S = (sum over d of q_f8 * k_f8, E4M3 products, fp32 accumulation) *
- * (s_q8 * s_k8 / sqrt(d)) on the FP8 matrix cores. */
+ * S = (sum over d of q_f8 * k_f8) * (s_q8 * s_k8 / sqrt(d)) on the FP8 matrix
+ * cores.  The E4M3 products are exact, but the matrix instruction does not
+ * sum them in full binary32: each 64-product step may be off by up to about
+ * 2^-11.5 of its largest product (measured), which matters only for blocks
+ * dominated by a few large products. */
 int tilemix_prefill_varlen3(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
                             const void* k_f16, const void* v_f16, const int8_t* q_i8, const int8_t* k_i8,
                             const float* q_scale, const float* k_scale, const uint8_t* q_f8,
