@@ -196,6 +196,19 @@ def test_headline_sampled(cov):
     _log("  err max/mean %.3e %.3e" % _check_rows(g["out"], ref["out"], cu, rows))
 
 
+@pytest.mark.parametrize("template", oracle.TEMPLATES)
+def test_sweep_l8k_sampled(template):
+    # the coverage/layout sweep shape (8 x 8192 tokens, Hq 24, Hkv 8, g = 2)
+    # at 50% for every template, on sampled query-tile rows
+    _log(f"llama3b L=8192 B=8 {template} 50% (sampled rows)")
+    q, k, v, cu, spec = synth.make_workload("llama3b_l8k")
+    g = run_gpu(q, k, v, cu, spec["hq"], spec["hkv"], template, 5000)
+    rows = _sampled_rows(cu, spec["hq"], [0, 11], seed=4, n_random=4)
+    ref = oracle.run(q, k, v, cu, spec["hq"], spec["hkv"], template, 5000, rows=rows)
+    assert np.array_equal(g["words"], ref["words"])
+    _log("  err max/mean %.3e %.3e" % _check_rows(g["out"], ref["out"], cu, rows))
+
+
 def test_qwen_varlen_sampled():
     _log("qwen2-7b varlen rowrandom 50% (sampled rows)")
     q, k, v, cu, spec = synth.make_workload("qwen2_7b_varlen")
