@@ -589,7 +589,8 @@ def main(argv=None):
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the TileMix path has no "
-              "cross-GPU work; the sharding design is described in DESIGN.md.", file=sys.stderr)
+              "cross-GPU work; splitting it across GPUs by KV head (or by query-tile rows for one long "
+              "sequence) is a design note, not implemented.", file=sys.stderr)
         return 2
 
     import numpy as np
