@@ -541,10 +541,20 @@ def cpu_baseline(q, k, v, cu, spec, template, coverage, budget_s=20.0):
     total_pairs = sum(int(L) * (int(L) + 1) // 2 for L in lens) * spec["hq"]
     t_total = t_prep + t_attn * total_pairs / pairs
     tokens = int(cu[-1])
+    # the whole oracle, unsampled, on the two small configurations
+    full = {}
+    import synth
+    for name in ("tiny", "llama3b_l1k"):
+        qs_, ks_, vs_, cs_, sp = synth.make_workload(name)
+        t1 = time.perf_counter()
+        oracle.run(qs_, ks_, vs_, cs_, sp["hq"], sp["hkv"], sp["template"], sp["coverage_bp"])
+        dt = time.perf_counter() - t1
+        full[name] = {"seconds": round(dt, 3), "tokens_per_s": int(cs_[-1]) / dt}
     return {"value": tokens / t_total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"routing + full quantiser pass ({t_prep:.1f}s) + {len(done)} of {len(units)} "
                        f"(sequence, head, query-tile) units of attention ({t_attn:.1f}s, "
-                       f"{pairs / total_pairs:.2%} of legal pairs), extrapolated by legal-pair count")}
+                       f"{pairs / total_pairs:.2%} of legal pairs), extrapolated by legal-pair count"),
+            "full_oracle": full}
 
 
 def main(argv=None):
