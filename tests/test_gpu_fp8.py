@@ -181,3 +181,48 @@ def test_fp8_lossless_inputs_give_plain_attention():
     from independent import naive_causal_attention
     ref = naive_causal_attention(q, k, v, cu, hq, hkv)
     assert_close_f8(out, ref, fp8_row_bound(q, k, v, cu, hq, hkv, tp, None))
+
+
+@pytest.mark.parametrize("c8,cf", [(5000, 2500), (0, 7500)])
+def test_three_path_headline_sampled(c8, cf):
+    # the 3B shape at 8 x 4096 tokens (outlier channels), SpTrans, at the two
+    # INT8 / FP8 mixes the three-path leg times; sampled work units, each
+    # row held to 4e-3 plus the derived FP8 bound
+    _log(f"three-path 3B L=4096 B=8 sptrans int8 {c8 / 100:.0f}% fp8 {cf / 100:.0f}% (sampled)")
+    q, k, v, cu, spec = synth.make_workload("llama3b_l4k")
+    hq, hkv, d = spec["hq"], spec["hkv"], spec["d"]
+    tp, out, _ = run3(q, k, v, cu, hq, hkv, "sptrans", c8, cf)
+    lens = [int(x) for x in np.diff(cu)]
+    w8, wf, *_ = oracle.routing_words3(lens, hkv, "sptrans", c8, cf)
+    assert np.array_equal(tp.words, w8) and np.array_equal(tp.words_f8, wf)
+    units = [(0, 0, 0), (0, 23, 31), (3, 11, 15), (7, 5, 31), (5, 17, 6)]
+    q_i8, qs = oracle.quantize_blocks(q, cu, 128)
+    k_i8, ks = oracle.quantize_blocks(k, cu, 64)
+    qf, qfs = oracle.quantize_blocks_fp8(q, cu, 128)
+    kf, kfs = oracle.quantize_blocks_fp8(k, cu, 64)
+    ref = oracle.prefill_attention3(q, k, v, q_i8, k_i8, qs, ks, qf, kf, qfs, kfs, w8, wf, cu, hq, hkv,
+                                    rows=units)
+    qv, kv_ = oracle.fp8_e4m3_decode(qf), oracle.fp8_e4m3_decode(kf)
+    grp = hq // hkv
+    for (s, h, r) in units:
+        L, a = lens[s], int(cu[s])
+        kvh = h // grp
+        geo = oracle.seq_geometry(L)
+        rows = np.arange(128 * r, min(128 * r + 128, L))
+        delta = np.zeros(len(rows))
+        for t in range(rows[-1] // 64 + 1):
+            G = t // geo.g
+            word = r + sum(oracle.seq_geometry(x).Tm for x in lens[:s])
+            if not ((int(wf[kvh, word]) >> G) & 1) or ((int(w8[kvh, word]) >> G) & 1):
+                continue
+            keys = np.arange(64 * t, min(64 * t + 64, L))
+            prod = np.abs(qv[a + rows, h][:, None, :] * kv_[a + keys, kvh][None, :, :])
+            steps = prod.reshape(len(rows), len(keys), -1, 64).max(axis=3).sum(axis=2)
+            steps = np.where(keys[None, :] <= rows[:, None], steps, 0.0)
+            scale = float(qfs[h, word]) * float(kfs[kvh, sum(oracle.seq_geometry(x).Tn for x in lens[:s]) + t])
+            delta = np.maximum(delta, EPS_F8 * steps.max(axis=1) * scale / np.sqrt(d))
+        vmax = np.maximum.accumulate(np.abs(v[a:a + L, kvh].astype(np.float64)).max(axis=1))[rows]
+        bound = (np.exp(2 * delta) - 1) * vmax
+        err = np.abs(out[a + rows, h].astype(np.float64) - ref[a + rows, h]).max(axis=1)
+        assert np.all(np.isfinite(out[a + rows, h]))
+        assert np.all(err <= MAX_ABS + bound), (s, h, r, float((err - MAX_ABS - bound).max()))
