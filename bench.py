@@ -4,7 +4,11 @@
                     [--template T] [--coverage BP] [--no-cpu-baseline]
 
 One step = one pass of the device hot path over one packed batch: the
-blockwise Q/K quantiser followed by the fused mixed-precision prefill kernel.
+blockwise K quantiser followed by the fused mixed-precision prefill kernel,
+which quantises each work unit's Q block in its prologue (one work unit is
+exactly one Q block).  ``breakdown.split_path`` times the same step as two
+passes over Q (the Q/K quantiser writing Q's INT8 codes, then the prefill
+reading them); both give bit-identical outputs.
 Routing words and the work plan are static per batch shape (the pages reuse
 one template across layers, batch entries and KV heads) and are built once,
 outside the timed region; their host build time is reported separately.
@@ -128,11 +132,11 @@ def write_traffic(args):
     """HBM bytes per prefill launch: FETCH_SIZE and WRITE_SIZE scaled by what
     the same counters read for a plain copy of known size."""
     fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.write_traffic
-    # the two-path kernel only (the FP8 leg's three-path kernel is
-    # prefill_kernel<d, true>)
+    # the step's prefill kernel, prefill_kernel<d, false, true> (two-path,
+    # Q quantised inline)
     kname = "tilemix::prefill_kernel"
-    fetch, nf = _counter_mean_kib(fetch_csv, (kname + "<", ", false>"))
-    write, nw = _counter_mean_kib(write_csv, (kname + "<", ", false>"))
+    fetch, nf = _counter_mean_kib(fetch_csv, (kname + "<", ", false, true>"))
+    write, nw = _counter_mean_kib(write_csv, (kname + "<", ", false, true>"))
     cfetch, _ = _counter_mean_kib(cfetch_csv, "copyBuffer")
     cwrite, _ = _counter_mean_kib(cwrite_csv, "copyBuffer")
     f_scale = args.copy_size / (cfetch * 1024)
@@ -199,7 +203,7 @@ def bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, steps):
     torch.cuda.synchronize()
     route_ms = (time.perf_counter() - t0) * 1e3
     out = torch.empty_like(qd)
-    attn_ms = time_in_pipeline(lambda: tp.quantize(qd, kd), lambda: tp.attend(qd, kd, vd, out), steps)
+    attn_ms = time_in_pipeline(lambda: tp.quantize_k(kd), lambda: tp.attend_qinline(qd, kd, vd, out), steps)
     P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
     t_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
     lens = np.diff(np.asarray(cu, dtype=np.int64))
@@ -314,8 +318,8 @@ def bench_depth(cu, hq, hkv, d, template, coverages, n_layers, seed=0, reps=10):
     ms = {
         "rms_norm": timed(lambda: tm.tilemix_stack_rms_norm(xt, u, hq, hkv, d, 1e-6)),
         "qkv_projection": timed(lambda: tm.tilemix_stack_qkv(u, wqkv_d[0], q, k, v, hq, hkv, d)),
-        "quantize": timed(lambda: tp.quantize(q, k)),
-        "prefill": timed(lambda: tp.attend(q, k, v, o)),
+        "quantize": timed(lambda: tp.quantize_k(k)),
+        "prefill": timed(lambda: tp.attend_qinline(q, k, v, o)),
         "out_projection_residual": timed(lambda: tm.tilemix_stack_out_residual(o, wo_d[0], xt, hq, hkv, d)),
     }
     # algorithmic bytes and flops of each kernel
@@ -324,7 +328,7 @@ def bench_depth(cu, hq, hkv, d, template, coverages, n_layers, seed=0, reps=10):
     qkv_b = T * C * 2 + (T * C + 2 * T * hkv * d) * 2 + hkv * (W + 2 * d) * W * 2
     out_f = 2 * T * W * W * hkv
     out_b = T * C * 2 + T * C * 8 + hkv * W * W * 2
-    quant_b = 3 * (T * hq * d + T * hkv * d) + 4 * (hq * tp.tq + hkv * tp.tk)
+    quant_b = 3 * T * hkv * d + 4 * hkv * tp.tk  # K only: Q is quantised inside the prefill
     P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
     attn_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
     roof = {"rms_norm": norm_b / PEAK_HBM,
@@ -375,9 +379,9 @@ def bench_sweep(workload, templates, coverages, steps=20):
     qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
     del q, k, v
     tp = tm.TileMixPrefill(cu, hq, hkv, d, templates[0], 0)
-    tp.quantize(qd, kd)
+    tp.quantize_k(kd)
     o_ref = torch.empty_like(qd)
-    tp.attend(qd, kd, vd, o_ref)  # 0%: no INT8 group, the same for every template
+    tp.attend_qinline(qd, kd, vd, o_ref)  # 0%: no INT8 group, the same for every template
     out = torch.empty_like(qd)
     tokens = int(cu[-1])
     res = {}
@@ -385,7 +389,7 @@ def bench_sweep(workload, templates, coverages, steps=20):
         rows = []
         for cov in coverages:
             tp.set_routing(template, cov)
-            ms = time_in_pipeline(lambda: tp.quantize(qd, kd), lambda: tp.attend(qd, kd, vd, out), steps)
+            ms = time_in_pipeline(lambda: tp.quantize_k(kd), lambda: tp.attend_qinline(qd, kd, vd, out), steps)
             mad = float((out.float() - o_ref.float()).abs().mean())
             P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
             t_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
@@ -561,7 +565,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3b_l4k")
     ap.add_argument("--template", default=None)
     ap.add_argument("--coverage", type=int, default=None, help="INT8 coverage in basis points")
@@ -636,8 +640,8 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
-        tp.quantize(qd, kd)
-        tp.attend(qd, kd, vd, out)
+        tp.quantize_k(kd)
+        tp.attend_qinline(qd, kd, vd, out)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -649,9 +653,9 @@ def main(argv=None):
     start.record(stream)
     for i in range(K):
         ev[i][0].record(stream)
-        tp.quantize(qd, kd)
+        tp.quantize_k(kd)
         ev[i][1].record(stream)
-        tp.attend(qd, kd, vd, out)
+        tp.attend_qinline(qd, kd, vd, out)
         ev[i][2].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -668,6 +672,10 @@ def main(argv=None):
     frac = t_roof / (attn_ms * 1e-3)
     flops_eq = t_roof * PEAK_F16
     achieved = flops_eq / (attn_ms * 1e-3) / 1e12
+    # the same step as two passes over Q (quantiser for Q and K, then the
+    # prefill reading Q's INT8 codes), timed right after
+    split_prefill_ms = time_in_pipeline(lambda: tp.quantize(qd, kd), lambda: tp.attend(qd, kd, vd, out), K)
+    split_quant_ms = time_in_pipeline(lambda: None, lambda: tp.quantize(qd, kd), K)
     traffic = None
     rec = traffic_record(os.path.join(ROOT, "profiles", f"prefill_{args.workload}_traffic.json"))
     if rec is not None:
@@ -698,7 +706,10 @@ def main(argv=None):
                       "int8_tops": 2 * d * P8 / (attn_ms * 1e-3) / 1e12,
                       "fp16_tflops": 2 * d * (2 * P - P8) / (attn_ms * 1e-3) / 1e12,
                       "roofline_us": t_roof * 1e6, "host_build_ms": host_build_ms,
-                      "wall_s": wall},
+                      "wall_s": wall,
+                      "split_path": {"quantize_ms": split_quant_ms, "prefill_ms": split_prefill_ms,
+                                     "ms_per_step": split_quant_ms + split_prefill_ms,
+                                     "prefill_frac": t_roof / (split_prefill_ms * 1e-3)}},
     }
     if not args.no_fp8:
         result["fp8"] = bench_fp8(qd, kd, vd, cu, hq, hkv, d, template, [(5000, 2500), (0, 7500)], 20)
@@ -716,8 +727,9 @@ def main(argv=None):
                                         20, not args.no_cpu_baseline)
     if any(k in result for k in ("fp8", "adaptive", "sweep", "depth", "decode")):
         # the headline kernel again, after the legs' seconds of sustained load
+        tp.set_routing(template, coverage)  # the adaptive leg leaves its own words
         result["breakdown"]["prefill_ms_after_legs"] = time_in_pipeline(
-            lambda: tp.quantize(qd, kd), lambda: tp.attend(qd, kd, vd, out), K)
+            lambda: tp.quantize_k(kd), lambda: tp.attend_qinline(qd, kd, vd, out), K)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, cu, spec, template, coverage, args.cpu_budget)
     else:

@@ -182,6 +182,27 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
                            const int8_t* k_i8, const float* q_scale, const float* k_scale,
                            const uint64_t* words_d, void* out_f16, void* hip_stream);
 
+/* Key half of tilemix_quantize_qk (device): the same K blocks, scales and
+ * codes, for use with tilemix_prefill_varlen_qinline.
+ * Inputs:  k_f16 [T, Hkv, d] (device).
+ * Outputs: k_i8 [T, Hkv, d] (device int8), k_scale float[Hkv][total_k_tiles]. */
+int tilemix_quantize_k(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, int8_t* k_i8,
+                       float* k_scale, void* hip_stream);
+
+/* tilemix_prefill_varlen with the Q quantisation done inside the kernel
+ * (device) -- [Digest, method]: each work unit covers exactly one Q block
+ * (128 rows of one query head), so it reduces that block's absmax across its
+ * waves and forms s_q = a / 127 and the INT8 codes in registers with the
+ * arithmetic of tilemix_quantize_qk.  The output equals, bit for bit, that of
+ * tilemix_quantize_qk followed by tilemix_prefill_varlen on the same inputs;
+ * Q's INT8 codes and scales are never written.  k_i8/k_scale from
+ * tilemix_quantize_k (or tilemix_quantize_qk).  Other arguments, layouts and
+ * errors as tilemix_prefill_varlen. */
+int tilemix_prefill_varlen_qinline(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                                   const void* k_f16, const void* v_f16, const int8_t* k_i8,
+                                   const float* k_scale, const uint64_t* words_d, void* out_f16,
+                                   void* hip_stream);
+
 /* INT8 key/value cache quantiser (device) -- [Explainer, 支持的场景]; [Digest,
  * setup]: the decode side keeps the cache in INT8.  Both K and V use the
  * prefill quantiser's key blocks: per (head, 64-row block of one sequence),
@@ -299,12 +320,13 @@ int tilemix_stack_out_residual(const void* o_f16, const void* wo_f16, float* x, 
                                int32_t hq, int32_t hkv, int32_t head_dim, void* hip_stream);
 
 /* Bytes of device workspace one tilemix_stack_layer call needs for this
- * plan (normalised input / attention output, Q, K, V, int8 codes and scales). */
+ * plan (normalised input / attention output, Q, K, V, K's int8 codes and
+ * scales). */
 int tilemix_stack_workspace_size(const int32_t* plan_h, int64_t* bytes);
 
 /* One layer in place on x (device float [T, Hq*d], T = the plan's tokens):
- * tilemix_stack_rms_norm, tilemix_stack_qkv, tilemix_quantize_qk,
- * tilemix_prefill_varlen with words_d ([Digest, method]: the same template
+ * tilemix_stack_rms_norm, tilemix_stack_qkv, tilemix_quantize_k,
+ * tilemix_prefill_varlen_qinline with words_d ([Digest, method]: the same template
  * words serve every layer), tilemix_stack_out_residual.  The workspace's
  * contents are overwritten; calls that share a workspace must not overlap. */
 int tilemix_stack_layer(const int32_t* plan_h, const int32_t* plan_d, const uint64_t* words_d, float* x,

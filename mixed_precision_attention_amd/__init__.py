@@ -54,6 +54,8 @@ _SIGNATURES = {
     "tilemix_build_plan": ([_P, _I32, _I32, _I32, _I32, _P, _I64], ctypes.c_int),
     "tilemix_quantize_qk": ([_P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "tilemix_prefill_varlen": ([_P] * 12, ctypes.c_int),
+    "tilemix_quantize_k": ([_P] * 6, ctypes.c_int),
+    "tilemix_prefill_varlen_qinline": ([_P] * 10, ctypes.c_int),
     "tilemix_debug_qk_i32_tile": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
     "tilemix_quantize_kv": ([_P] * 9, ctypes.c_int),
     "tilemix_build_routing3": ([_P, _I32, _I32, _I32, _I32, _I32, _U64, _P, _P, _P, _P, _P, _P], ctypes.c_int),
@@ -214,6 +216,22 @@ def tilemix_prefill_varlen(plan_h, plan_d, q, k, v, q_i8, k_i8, q_scale, k_scale
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
         _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(q_i8, torch.int8, "q_i8"),
         _dptr(k_i8, torch.int8, "k_i8"), _dptr(q_scale, torch.float32, "q_scale"),
+        _dptr(k_scale, torch.float32, "k_scale"), _dptr(words_d, torch.int64, "words_d"),
+        _dptr(out, torch.float16, "out"), _stream(stream)))
+
+
+def tilemix_quantize_k(plan_h, plan_d, k, k_i8, k_scale, stream=None):
+    import torch
+    _check(lib().tilemix_quantize_k(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(k, torch.float16, "k"),
+        _dptr(k_i8, torch.int8, "k_i8"), _dptr(k_scale, torch.float32, "k_scale"), _stream(stream)))
+
+
+def tilemix_prefill_varlen_qinline(plan_h, plan_d, q, k, v, k_i8, k_scale, words_d, out, stream=None):
+    import torch
+    _check(lib().tilemix_prefill_varlen_qinline(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
+        _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(k_i8, torch.int8, "k_i8"),
         _dptr(k_scale, torch.float32, "k_scale"), _dptr(words_d, torch.int64, "words_d"),
         _dptr(out, torch.float16, "out"), _stream(stream)))
 
@@ -385,6 +403,16 @@ class TileMixPrefill:
     def attend(self, q, k, v, out, stream=None):
         tilemix_prefill_varlen(self.plan_h, self.plan_d, q, k, v, self.q_i8, self.k_i8,
                                self.q_scale, self.k_scale, self.words_d, out, stream)
+
+    def quantize_k(self, k, stream=None):
+        """The key half of ``quantize`` (for ``attend_qinline``)."""
+        tilemix_quantize_k(self.plan_h, self.plan_d, k, self.k_i8, self.k_scale, stream)
+
+    def attend_qinline(self, q, k, v, out, stream=None):
+        """``attend`` with Q quantised inside the prefill kernel; needs the
+        key codes of ``quantize_k`` (or ``quantize``)."""
+        tilemix_prefill_varlen_qinline(self.plan_h, self.plan_d, q, k, v, self.k_i8, self.k_scale,
+                                       self.words_d, out, stream)
 
     def __call__(self, q, k, v, out=None, stream=None):
         import torch

@@ -71,6 +71,18 @@ __device__ inline int find_seq(const int32_t* seqtab, int batch, int field, int 
   return lo;
 }
 
+// q = round-half-even(fl32(x / s)) clamped to [-127, 127].  x * fl32(1 / s)
+// is within 2.3e-5 of fl32(x / s) for |x / s| <= 127 (two roundings of 2^-24
+// relative each plus half an ulp of the quotient), so it rounds to the same
+// integer unless it lies within 2^-15 of a half-integer; only those elements
+// take the exact IEEE division.  rs = fl32(1 / s), or 0 when s = 0.
+__device__ inline int quant_code_i8(float x, float rs, float s) {
+  const float y = x * rs;
+  float qf = __builtin_rintf(y);
+  if (__builtin_fabsf(y - qf) > 0.5f - 0x1p-15f) qf = __builtin_rintf(__fdiv_rn(x, s));
+  return (int)__builtin_amdgcn_fmed3f(qf, -127.f, 127.f);
+}
+
 template <int D, int BLK>
 __device__ inline void quantize_block(const _Float16* src, int8_t* dst, float* scale_out,
                                       int row_stride, int nrows, float* red) {
@@ -97,11 +109,6 @@ __device__ inline void quantize_block(const _Float16* src, int8_t* dst, float* s
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = __fdiv_rn(amax, 127.0f);
   if (tid == 0) *scale_out = s;
-  // q = round-half-even(fl32(x / s)).  x * fl32(1 / s) is within 2.3e-5 of
-  // fl32(x / s) for |x / s| <= 127 (two roundings of 2^-24 relative each plus
-  // half an ulp of the quotient), so it rounds to the same integer unless it
-  // lies within 2^-15 of a half-integer; only those elements take the exact
-  // IEEE division.
   const float rs = amax > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
@@ -111,12 +118,7 @@ __device__ inline void quantize_block(const _Float16* src, int8_t* dst, float* s
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float x = (float)vals[i][j];
-      const float y = x * rs;
-      float qf = __builtin_rintf(y);
-      if (__builtin_fabsf(y - qf) > 0.5f - 0x1p-15f) qf = __builtin_rintf(__fdiv_rn(x, s));
-      const int qv = (int)__builtin_amdgcn_fmed3f(qf, -127.f, 127.f);
-      const uint32_t b = (uint32_t)(qv & 0xff);
+      const uint32_t b = (uint32_t)(quant_code_i8((float)vals[i][j], rs, s) & 0xff);
       if (j < 4) lo |= b << (8 * j); else hi |= b << (8 * (j - 4));
     }
     *reinterpret_cast<uint2*>(dst + (size_t)r * row_stride + cc * 8) = make_uint2(lo, hi);
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void quantize_qk_kernel(QuantArgs a) {
   __shared__ float red[4];
   const int32_t* seqtab = a.plan + kHeaderLen;
   int bid = blockIdx.x;
-  const int nq = a.tq * a.hq;
+  const int nq = a.q ? a.tq * a.hq : 0;  // no Q pointer: the key blocks only
   if (bid < nq) {
     const int tile = bid / a.hq, head = bid % a.hq;
     const int s = find_seq(seqtab, a.batch, kSeqQtOff, tile);
@@ -328,6 +330,7 @@ struct Tile {
   static constexpr int kScales = 1024;  // key-tile scales staged per chunk
   static constexpr int kLds = 2 * kBuf + kScales * 4;
   static constexpr int kLds3 = kLds + kScales * 4;  // + the FP8 key-tile scales
+  static constexpr int kLdsQ = kLds + 16;             // + the Q absmax exchange
 };
 
 // Combine a value with the same register of lane l ^ 32 (no LDS round trip).
@@ -473,6 +476,83 @@ __device__ inline void load_q(const _Float16* qrow, const int8_t* q8row, bool va
   }
 }
 
+// The work unit's Q block quantised in registers ([Digest, method]: Q blocks
+// of 128 x d, s = absmax / 127, the quantiser's arithmetic element for
+// element).  qf holds this lane's fp16 fragments (zeros for rows past the
+// sequence end, which leave the absmax unchanged); red is 4 floats of LDS.
+// Codes are made in the fp16 fragment order (lane half hh holds dims
+// 16 kk + 8 hh + 0..7) and moved into the INT8 one (dims 32 kk + 16 hh +
+// 0..15) by one exchange per dword with lane l ^ 32.  Returns the scale.
+template <int D>
+__device__ inline float quantize_q_inline(const half8* qf, int4v* qb, float* red, int w) {
+  const int lane = threadIdx.x & 63;
+  half2v m2[4] = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half2v p = {qf[kk][2 * j], qf[kk][2 * j + 1]};
+      m2[j] = __builtin_elementwise_max(m2[j], __builtin_elementwise_abs(p));
+    }
+  m2[0] = __builtin_elementwise_max(__builtin_elementwise_max(m2[0], m2[1]), __builtin_elementwise_max(m2[2], m2[3]));
+  float amax = fmaxf((float)m2[0][0], (float)m2[0][1]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (lane == 0) red[w] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(amax, 127.0f);
+  const float rs = amax > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  // Straight-line pass: t = fl(x * rs + 1.5 * 2^23) rounds the exact product
+  // p = x * rs (|p| <= 127 + tiny) half-to-even to the integer t - 1.5 * 2^23,
+  // whose low byte is the low byte of t's bits; e = p - code (to 2^-25).  p
+  // lies within 1.2e-5 of fl(x / s) (rs's rounding plus half an ulp of the
+  // quotient), so the code equals round-half-even(fl(x / s)) unless |e| >
+  // 0.5 - 2^-16.  A wave with such an element redoes its block row with
+  // quant_code_i8, element for element.
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  uint32_t cw[D / 16][2];
+  float emax = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = (float)qf[kk][4 * h + j];
+        const float t = __builtin_fmaf(x, rs, kMagic);
+        const float e = __builtin_fmaf(x, rs, kMagic - t);
+        emax = fmaxf(emax, __builtin_fabsf(e));
+        b[j] = __builtin_bit_cast(uint32_t, t);
+      }
+      cw[kk][h] = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+    }
+  if (__builtin_amdgcn_ballot_w64(emax > 0.5f - 0x1p-16f)) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          word |= (uint32_t)(quant_code_i8((float)qf[kk][4 * h + j], rs, s) & 0xff) << (8 * j);
+        cw[kk][h] = word;
+      }
+  }
+  // Lanes 32..63 of the first operand trade places with lanes 0..31 of the
+  // second: the low half keeps its own dims 32 kk2 + 0..7 and receives the
+  // high half's 8..15; the high half receives the low half's 16..23 and keeps
+  // its own 24..31.
+#pragma unroll
+  for (int kk2 = 0; kk2 < D / 32; ++kk2) {
+    const auto r0 = __builtin_amdgcn_permlane32_swap(cw[2 * kk2][0], cw[2 * kk2 + 1][0], false, false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(cw[2 * kk2][1], cw[2 * kk2 + 1][1], false, false);
+    qb[kk2] = (int4v){(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
+  }
+  return s;
+}
+
 // --------------------------------------------------------------------------
 // Fused mixed-precision prefill.  One workgroup = one work unit (sequence,
 // query head, 128-row query tile); wave w owns queries 32w .. 32w+31.
@@ -568,11 +648,14 @@ __device__ __forceinline__ void tile_step(const char* buf, int code, float f_i8,
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, accf[kb][i]);
   mx = max_with_other_half(mx);
   mx = (mx == -INFINITY) ? -INFINITY : mx * f;
-  const bool raise = mx > st.m + kLazy;
-  const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - mx) : 1.0f;
-  st.m = raise ? mx : st.m;
-  st.lsum *= alpha;
-  if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rescale O where a lane raised
+  // Wave-uniform: when some row's maximum has outgrown m by more than kLazy,
+  // the wave rescales O anyway, so every row whose tile maximum exceeds its m
+  // takes it now (fewer later rescales; P <= 2^kLazy still holds).
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kLazy)) {
+    const float mnew = fmaxf(st.m, mx);
+    const float alpha = mnew == st.m ? 1.0f : __builtin_amdgcn_exp2f(st.m - mnew);
+    st.m = mnew;
+    st.lsum *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
   }
@@ -635,8 +718,11 @@ __device__ __forceinline__ void tile_step(const char* buf, int code, float f_i8,
 
 // kThree adds the FP8 path: a second word per (KV head, row) marks FP8
 // groups (never also INT8); without it the kernel is the two-path one.
-template <int D, bool kThree>
+// kQInline (two-path only): the unit's Q block is quantised in the prologue
+// instead of read from the quantiser's output (a.qi8, a.qs unused).
+template <int D, bool kThree, bool kQInline = false>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+  static_assert(!(kThree && kQInline), "inline Q quantisation is a two-path variant");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   using T = Tile<D>;
 
@@ -683,8 +769,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   half8 qf[D / 16];
   int4v qb[D / 32];
-  load_q<D>(a.q + ((size_t)(start + qi) * a.hq + head) * D,
-            a.qi8 + ((size_t)(start + qi) * a.hq + head) * D, qvalid, qf, qb);
+  if (!kQInline)
+    load_q<D>(a.q + ((size_t)(start + qi) * a.hq + head) * D,
+              a.qi8 + ((size_t)(start + qi) * a.hq + head) * D, qvalid, qf, qb);
   int8v qc[kThree ? D / 64 : 1];  // FP8 query codes: 32 per lane per 64-wide step
   if (kThree) {
     const uint8_t* qrow = a.qf8 + ((size_t)(start + qi) * a.hq + head) * D;
@@ -702,7 +789,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // asm-issued tile loads, so a wait it placed later for these would also
   // wait for every tile load in flight.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  const float sq = load_uniform(a.qs + (size_t)head * a.tq + qt_off + row);
+  float sq;
+  if (kQInline) {
+    const _Float16* qrow = a.q + ((size_t)(start + qi) * a.hq + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      half8 v = {};
+      if (qvalid) v = *reinterpret_cast<const half8*>(qrow + kk * 16 + (lane >> 5) * 8);
+      qf[kk] = v;
+    }
+    float* red = reinterpret_cast<float*>(smem + 2 * T::kBuf) + T::kScales;
+    const float s = quantize_q_inline<D>(qf, qb, red, w);
+    sq = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s)));
+  } else {
+    sq = load_uniform(a.qs + (size_t)head * a.tq + qt_off + row);
+  }
   const float sqf = kThree ? load_uniform(a.qsf8 + (size_t)head * a.tq + qt_off + row) : 0.f;
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
   const float scale16 = inv_sqrt_d * kLog2e;
@@ -915,6 +1016,86 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
     hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(grid), dim3(kThreads), Tile<128>::kLds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return TILEMIX_OK;
+}
+
+int tilemix_quantize_k(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, int8_t* k_i8,
+                       float* k_scale, void* hip_stream) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const bool any = plan_h[kTotalTokens] > 0;
+  if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(k_f16, "k_f16", any)) ||
+      (rc = check_dev_ptr(k_i8, "k_i8", any)) || (rc = check_dev_ptr(k_scale, "k_scale", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  QuantArgs a;
+  a.plan = plan_d;
+  a.q = nullptr;  // key blocks only
+  a.k = static_cast<const _Float16*>(k_f16);
+  a.qi8 = nullptr;
+  a.ki8 = k_i8;
+  a.qs = nullptr;
+  a.ks = k_scale;
+  a.hq = plan_h[kHq];
+  a.hkv = plan_h[kHkv];
+  a.batch = plan_h[kBatch];
+  a.tq = plan_h[kTotalQTiles];
+  a.tk = plan_h[kTotalKTiles];
+  const int64_t blocks = (int64_t)a.tk * a.hkv;
+  if (blocks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (plan_h[kHeadDim] == 64)
+    hipLaunchKernelGGL(quantize_qk_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(quantize_qk_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "quantize_k launch");
+  return TILEMIX_OK;
+}
+
+int tilemix_prefill_varlen_qinline(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                                   const void* k_f16, const void* v_f16, const int8_t* k_i8,
+                                   const float* k_scale, const uint64_t* words_d, void* out_f16,
+                                   void* hip_stream) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const bool any = plan_h[kNumItems] > 0;
+  if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
+      (rc = check_dev_ptr(k_f16, "k_f16", any)) || (rc = check_dev_ptr(v_f16, "v_f16", any)) ||
+      (rc = check_dev_ptr(k_i8, "k_i8", any)) || (rc = check_dev_ptr(k_scale, "k_scale", any)) ||
+      (rc = check_dev_ptr(words_d, "words_d", any)) || (rc = check_dev_ptr(out_f16, "out_f16", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  PrefillArgs a;
+  a.plan = plan_d;
+  a.q = static_cast<const _Float16*>(q_f16);
+  a.k = static_cast<const _Float16*>(k_f16);
+  a.v = static_cast<const _Float16*>(v_f16);
+  a.qi8 = nullptr;  // Q is quantised in the kernel
+  a.ki8 = k_i8;
+  a.qs = nullptr;
+  a.ks = k_scale;
+  a.words = words_d;
+  a.out = static_cast<_Float16*>(out_f16);
+  a.qf8 = nullptr;
+  a.kf8 = nullptr;
+  a.qsf8 = nullptr;
+  a.ksf8 = nullptr;
+  a.wordsf8 = nullptr;
+  a.hq = plan_h[kHq];
+  a.hkv = plan_h[kHkv];
+  a.tq = plan_h[kTotalQTiles];
+  a.tk = plan_h[kTotalKTiles];
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const unsigned grid = (unsigned)plan_h[kNumItems];
+  if (plan_h[kHeadDim] == 64)
+    hipLaunchKernelGGL((prefill_kernel<64, false, true>), dim3(grid), dim3(kThreads), Tile<64>::kLdsQ, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<128, false, true>), dim3(grid), dim3(kThreads), Tile<128>::kLdsQ, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "prefill_qinline launch");
   return TILEMIX_OK;
 }
 

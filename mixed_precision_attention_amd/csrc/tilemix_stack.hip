@@ -364,7 +364,7 @@ int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
 // output once the projection has read it), Q, K, V, their int8 codes and
 // scales, each at a 256-byte boundary.
 struct LayerWs {
-  int64_t uo, q, k, v, qi, ki, qs, ks, total;
+  int64_t uo, q, k, v, ki, ks, total;
 };
 
 LayerWs layer_ws(const int32_t* plan_h) {
@@ -379,12 +379,8 @@ LayerWs layer_ws(const int32_t* plan_h) {
   off += align256(T * hkv * d * 2);
   w.v = off;
   off += align256(T * hkv * d * 2);
-  w.qi = off;
-  off += align256(T * hq * d);
   w.ki = off;
   off += align256(T * hkv * d);
-  w.qs = off;
-  off += align256(hq * (int64_t)plan_h[kTotalQTiles] * 4);
   w.ks = off;
   off += align256(hkv * (int64_t)plan_h[kTotalKTiles] * 4);
   w.total = off;
@@ -476,16 +472,14 @@ int tilemix_stack_layer(const int32_t* plan_h, const int32_t* plan_d, const uint
   _Float16* q = reinterpret_cast<_Float16*>(ws + w.q);
   _Float16* k = reinterpret_cast<_Float16*>(ws + w.k);
   _Float16* v = reinterpret_cast<_Float16*>(ws + w.v);
-  int8_t* qi = reinterpret_cast<int8_t*>(ws + w.qi);
   int8_t* ki = reinterpret_cast<int8_t*>(ws + w.ki);
-  float* qs = reinterpret_cast<float*>(ws + w.qs);
   float* ks = reinterpret_cast<float*>(ws + w.ks);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if ((rc = launch_norm(x, uo, T, hq, hkv, d, eps, st))) return rc;
   if ((rc = launch_proj(false, uo, static_cast<const _Float16*>(wqkv_f16), q, k, v, nullptr, T, hq, hkv, d, st)))
     return rc;
-  if ((rc = tilemix_quantize_qk(plan_h, plan_d, q, k, qi, ki, qs, ks, hip_stream))) return rc;
-  if ((rc = tilemix_prefill_varlen(plan_h, plan_d, q, k, v, qi, ki, qs, ks, words_d, uo, hip_stream))) return rc;
+  if ((rc = tilemix_quantize_k(plan_h, plan_d, k, ki, ks, hip_stream))) return rc;
+  if ((rc = tilemix_prefill_varlen_qinline(plan_h, plan_d, q, k, v, ki, ks, words_d, uo, hip_stream))) return rc;
   return launch_proj(true, uo, static_cast<const _Float16*>(wo_f16), nullptr, nullptr, nullptr, x, T, hq, hkv, d,
                      st);
 }

@@ -134,6 +134,10 @@ def test_errors_are_reported():
     assert lib.tilemix_prefill_varlen(ctypes.c_void_p(bad.ctypes.data), fake, fake, fake, fake, fake, fake,
                                       fake, fake, fake, fake, None) == -1
     assert "not a TileMix plan" in tm.tilemix_last_error()
+    assert lib.tilemix_quantize_k(p, fake, fake, odd, fake, None) == -1
+    assert "k_i8" in tm.tilemix_last_error() and "aligned" in tm.tilemix_last_error()
+    assert lib.tilemix_prefill_varlen_qinline(p, fake, fake, fake, fake, fake, None, fake, fake, None) == -1
+    assert "k_scale is NULL" in tm.tilemix_last_error()
     assert lib.tilemix_debug_qk_i32_tile(p, fake, fake, fake, 0, 0, 5, 0, fake, None) == -1
     assert "row" in tm.tilemix_last_error()
     bad = plan.copy()
@@ -225,6 +229,8 @@ def test_empty_batch_is_a_no_op():
     # nothing to launch: returns OK without touching device pointers
     assert lib.tilemix_prefill_varlen(p, fake, None, None, None, None, None, None, None, None, None, None) == 0
     assert lib.tilemix_quantize_qk(p, fake, None, None, None, None, None, None, None) == 0
+    assert lib.tilemix_quantize_k(p, fake, None, None, None, None) == 0
+    assert lib.tilemix_prefill_varlen_qinline(p, fake, None, None, None, None, None, None, None, None) == 0
 
 
 # ------------------------------------------------------- multi-layer stack
@@ -237,8 +243,8 @@ def test_stack_workspace_size():
 
     def a256(n):
         return -(-n // 256) * 256
-    want = (2 * a256(T * hq * d * 2) + 2 * a256(T * hkv * d * 2) + a256(T * hq * d) + a256(T * hkv * d)
-            + a256(hq * tq * 4) + a256(hkv * tk * 4))
+    # fp16 staging for (norm out / attention out), Q, K, V; K's codes and scales
+    want = 2 * a256(T * hq * d * 2) + 2 * a256(T * hkv * d * 2) + a256(T * hkv * d) + a256(hkv * tk * 4)
     assert tm.tilemix_stack_workspace_size(plan) == want
 
 
