@@ -35,7 +35,7 @@ statistic, the host ranking, and the prefill under the resulting words at the
 same coverage.
 
 ``sweep_headline`` and ``sweep`` (skip with --no-sweep) time the fused
-prefill at INT8 coverages 0, 10, 25, 50, 75 and 100% -- the headline
+prefill (the better of two passes) at INT8 coverages 0, 10, 25, 50, 75 and 100% -- the headline
 workload's template, then every template at L=8192 -- with tokens/s, the
 roofline fraction, whether tokens/s is non-decreasing in coverage, and
 MAD(c), the mean absolute difference of all fp16 outputs from the same
@@ -387,9 +387,20 @@ def bench_sweep(workload, templates, coverages, steps=20):
     res = {}
     for template in templates:
         rows = []
+        # two passes over the coverages, the better time of each kept:
+        # consecutive configurations differ by a few percent, about the
+        # spread of one timing
+        best = {}
+        for _ in range(2):
+            for cov in coverages:
+                tp.set_routing(template, cov)
+                ms = time_in_pipeline(lambda: tp.quantize_k(kd), lambda: tp.attend_qinline(qd, kd, vd, out), steps)
+                best[cov] = min(best.get(cov, ms), ms)
         for cov in coverages:
             tp.set_routing(template, cov)
-            ms = time_in_pipeline(lambda: tp.quantize_k(kd), lambda: tp.attend_qinline(qd, kd, vd, out), steps)
+            tp.quantize_k(kd)
+            tp.attend_qinline(qd, kd, vd, out)
+            ms = best[cov]
             mad = float((out.float() - o_ref.float()).abs().mean())
             P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
             t_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
