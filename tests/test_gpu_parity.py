@@ -276,3 +276,34 @@ def test_lossless_inputs_coverage_independent(d):
     for template, cov in (("band", 5000), ("rowrandom", 2500), ("sptrans", 10000)):
         assert np.array_equal(run_gpu(q, k, v, cu, hq, hkv, template, cov)["out"], base), (template, cov)
     assert_close(base, naive_causal_attention(q, k, v, cu, hq, hkv))
+
+
+@pytest.mark.parametrize("cov", [0, 5000, 10000])
+def test_running_max_ramps(cov):
+    # Scores that grow linearly along the keys at a per-row rate of 10, 20,
+    # -10 or 5 log2 units per 64-key tile (rows interleaved, so one wave holds
+    # every rate): the rows at 20 push the running maximum past the lazy
+    # margin on every tile, the rows at 10 and 5 only every second or third
+    # tile on their own (then they take their tile maximum with the wave's
+    # rescale), the falling rows never after their first tile.
+    _log(f"running-max ramps cov={cov}")
+    lens, hq, hkv, d = [1024, 300], 2, 1, 64
+    T = sum(lens)
+    rng = np.random.default_rng(41)
+    b = 10.0 * np.sqrt(d) / (64 * np.log2(np.e))  # 10 log2 units per tile at rate 1
+    rate = np.array([1.0, 2.0, -1.0, 0.5])
+    q = np.zeros((T, hq, d), dtype=np.float16)
+    k = np.zeros((T, hkv, d), dtype=np.float16)
+    off = 0
+    for L in lens:
+        j = np.arange(L)
+        q[off:off + L, :, 0] = rate[j % 4][:, None]
+        q[off:off + L, :, 1:] = rng.normal(0, 0.05, (L, hq, d - 1))
+        k[off:off + L, 0, 0] = b * j
+        k[off:off + L, 0, 1:] = rng.normal(0, 0.05, (L, d - 1))
+        off += L
+    v = rng.normal(0, 1, (T, hkv, d)).astype(np.float16)
+    cu = synth.cu_seqlens_of(lens)
+    g = run_gpu(q, k, v, cu, hq, hkv, "band", cov)
+    ref = oracle.run(q, k, v, cu, hq, hkv, "band", cov)
+    assert_close(g["out"], ref["out"])
