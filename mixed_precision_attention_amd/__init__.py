@@ -414,12 +414,21 @@ class TileMixPrefill:
         tilemix_prefill_varlen_qinline(self.plan_h, self.plan_d, q, k, v, self.k_i8, self.k_scale,
                                        self.words_d, out, stream)
 
-    def __call__(self, q, k, v, out=None, stream=None):
+    def __call__(self, q, k, v, out=None, stream=None, inline_q: bool = False):
+        """One prefill step.  By default the quantiser writes Q's and K's
+        codes (kept in ``q_i8``/``k_i8`` and the scales) and the prefill reads
+        them; ``inline_q=True`` quantises K alone and lets the prefill quantise
+        each Q block in registers (the same output, bit for bit, and faster;
+        ``q_i8``/``q_scale`` are then left untouched)."""
         import torch
         if out is None:
             out = torch.empty_like(q)
-        self.quantize(q, k, stream)
-        self.attend(q, k, v, out, stream)
+        if inline_q:
+            self.quantize_k(k, stream)
+            self.attend_qinline(q, k, v, out, stream)
+        else:
+            self.quantize(q, k, stream)
+            self.attend(q, k, v, out, stream)
         return out
 
 
@@ -445,6 +454,13 @@ class TileMixPrefill3(TileMixPrefill):
         for name, w in (("words_d", self.words), ("words_f8_d", self.words_f8)):
             w = w if w.size else np.zeros((1, 1), dtype=np.uint64)
             setattr(self, name, torch.from_numpy(w.view(np.int64)).to(self.device))
+
+    def quantize_k(self, k, stream=None):
+        raise TileMixError(-2, "the three-path prefill reads Q's INT8 and FP8 codes from its quantisers; "
+                               "inline Q quantisation is a two-path variant")
+
+    def attend_qinline(self, q, k, v, out, stream=None):
+        self.quantize_k(k, stream)
 
     def quantize(self, q, k, stream=None):
         super().quantize(q, k, stream)

@@ -276,3 +276,12 @@ def test_stack_argument_validation():
     need = tm.tilemix_stack_workspace_size(plan)
     rc = lib.tilemix_stack_layer(tm._hptr(plan), fake, fake, fake, fake, fake, 1e-6, fake, need - 1, None)
     assert rc == -1 and "workspace" in tm.tilemix_last_error()
+
+
+def test_three_path_rejects_inline_q():
+    # the inline-Q prefill is a two-path kernel: the three-path object refuses
+    # it before touching any buffer
+    tp = tm.TileMixPrefill3.__new__(tm.TileMixPrefill3)
+    with pytest.raises(tm.TileMixError, match="two-path") as e:
+        tp(None, None, None, out=object(), inline_q=True)
+    assert e.value.code == -2

@@ -33,9 +33,8 @@ def both_paths(q, k, v, cu, hq, hkv, template, cov, seed=0):
     k_scale = tp.k_scale.clone()
     tp.k_i8.fill_(0x55)
     tp.k_scale.fill_(float("nan"))
-    tp.quantize_k(kd)
     out = torch.full_like(qd, float("nan"))
-    tp.attend_qinline(qd, kd, vd, out)
+    tp(qd, kd, vd, out, inline_q=True)
     torch.cuda.synchronize()
     T = q.shape[0]
     assert torch.equal(tp.k_i8[:T], k_i8[:T])
