@@ -220,32 +220,43 @@ def bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, steps):
 
 def bench_fp8(qd, kd, vd, cu, hq, hkv, d, template, mixes, steps):
     """Three-path prefill (FP16 / FP8 / INT8 groups) at the given (INT8, FP8)
-    coverages: FP8 quantiser time and the prefill kernel against the
-    three-precision MFMA roofline (FP8 at the published dense peak)."""
+    coverages against the three-precision MFMA roofline (FP8 at the published
+    dense peak), as a step like the headline's (both key quantisers, then the
+    prefill making Q's INT8 and FP8 codes in its prologue) and as
+    ``split_path`` (both Q/K quantisers, then the prefill reading Q's codes)."""
     import torch
     import mixed_precision_attention_amd as tm
     stream = torch.cuda.current_stream()
     out = torch.empty_like(qd)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
     rows = []
     for c8, cf in mixes:
         tp = tm.TileMixPrefill3(cu, hq, hkv, d, template, c8, cf)
-        tp.quantize(qd, kd)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            tm.tilemix_quantize_qk_fp8(tp.plan_h, tp.plan_d, qd, kd, tp.q_f8, tp.k_f8, tp.q_scale_f8,
-                                       tp.k_scale_f8)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        q8_us = e0.elapsed_time(e1) * 1e3 / steps
-        ms = time_in_pipeline(lambda: tp.quantize(qd, kd), lambda: tp.attend(qd, kd, vd, out), steps)
+        kq_us = timed(lambda: tp.quantize_k(kd))
+        qk_us = timed(lambda: tp.quantize(qd, kd))
+        ms = time_in_pipeline(lambda: tp.quantize_k(kd), lambda: tp.attend_qinline(qd, kd, vd, out), steps)
+        ms_split = time_in_pipeline(lambda: tp.quantize(qd, kd), lambda: tp.attend(qd, kd, vd, out), steps)
         P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
         _, Pf = legal_pair_counts(cu, tp.words_f8, hq, hkv)
         t_roof = 2 * d * (P - P8 - Pf) / PEAK_F16 + 2 * d * P8 / PEAK_I8 + 2 * d * Pf / PEAK_F8 \
             + 2 * d * P / PEAK_F16
         rows.append({"int8_bp": c8, "fp8_bp": cf, "prefill_ms": ms, "frac": t_roof / (ms * 1e-3),
-                     "int8_pair_share": P8 / P, "fp8_pair_share": Pf / P, "fp8_quantize_us": q8_us})
+                     "key_quantize_us": kq_us, "step_ms": ms + kq_us * 1e-3,
+                     "int8_pair_share": P8 / P, "fp8_pair_share": Pf / P,
+                     "split_path": {"prefill_ms": ms_split, "frac": t_roof / (ms_split * 1e-3),
+                                    "quantize_us": qk_us, "step_ms": ms_split + qk_us * 1e-3}})
     return {"template": template, "runs": rows}
 
 

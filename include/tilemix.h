@@ -239,6 +239,26 @@ int tilemix_prefill_varlen3(const int32_t* plan_h, const int32_t* plan_d, const 
                             const uint64_t* words_i8_d, const uint64_t* words_f8_d, void* out_f16,
                             void* hip_stream);
 
+/* Key half of tilemix_quantize_qk_fp8 (device): the same K blocks, scales
+ * and codes, for use with tilemix_prefill_varlen3_qinline.
+ * Outputs: k_f8 [T, Hkv, d] (device bytes), k_scale_f8 float[Hkv][total_k_tiles]. */
+int tilemix_quantize_k_fp8(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, uint8_t* k_f8,
+                           float* k_scale_f8, void* hip_stream);
+
+/* tilemix_prefill_varlen3 with Q's INT8 and FP8 codes made inside the kernel
+ * (device), one Q block per work unit as in tilemix_prefill_varlen_qinline:
+ * the INT8 codes with the arithmetic of tilemix_quantize_qk and the E4M3 codes
+ * with that of tilemix_quantize_qk_fp8, from the one block absmax.  The
+ * output equals, bit for bit, that of the two quantisers followed by
+ * tilemix_prefill_varlen3.  K's codes from tilemix_quantize_k and
+ * tilemix_quantize_k_fp8 (or the Q/K quantisers).  Other arguments, layouts
+ * and errors as tilemix_prefill_varlen3. */
+int tilemix_prefill_varlen3_qinline(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                                    const void* k_f16, const void* v_f16, const int8_t* k_i8,
+                                    const float* k_scale, const uint8_t* k_f8, const float* k_scale_f8,
+                                    const uint64_t* words_i8_d, const uint64_t* words_f8_d, void* out_f16,
+                                    void* hip_stream);
+
 /* Bytes of device workspace tilemix_decode_varlen needs for this plan:
  * B * Hq * ceil(max L / 256) * (d + 2) * 4. */
 int tilemix_decode_workspace_size(const int32_t* plan_h, int64_t* bytes);

@@ -56,6 +56,8 @@ _SIGNATURES = {
     "tilemix_prefill_varlen": ([_P] * 12, ctypes.c_int),
     "tilemix_quantize_k": ([_P] * 6, ctypes.c_int),
     "tilemix_prefill_varlen_qinline": ([_P] * 10, ctypes.c_int),
+    "tilemix_quantize_k_fp8": ([_P] * 6, ctypes.c_int),
+    "tilemix_prefill_varlen3_qinline": ([_P] * 13, ctypes.c_int),
     "tilemix_debug_qk_i32_tile": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
     "tilemix_quantize_kv": ([_P] * 9, ctypes.c_int),
     "tilemix_build_routing3": ([_P, _I32, _I32, _I32, _I32, _I32, _U64, _P, _P, _P, _P, _P, _P], ctypes.c_int),
@@ -234,6 +236,24 @@ def tilemix_prefill_varlen_qinline(plan_h, plan_d, q, k, v, k_i8, k_scale, words
         _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(k_i8, torch.int8, "k_i8"),
         _dptr(k_scale, torch.float32, "k_scale"), _dptr(words_d, torch.int64, "words_d"),
         _dptr(out, torch.float16, "out"), _stream(stream)))
+
+
+def tilemix_quantize_k_fp8(plan_h, plan_d, k, k_f8, k_scale_f8, stream=None):
+    import torch
+    _check(lib().tilemix_quantize_k_fp8(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(k, torch.float16, "k"),
+        _dptr(k_f8, torch.uint8, "k_f8"), _dptr(k_scale_f8, torch.float32, "k_scale_f8"), _stream(stream)))
+
+
+def tilemix_prefill_varlen3_qinline(plan_h, plan_d, q, k, v, k_i8, k_scale, k_f8, k_scale_f8, words_i8_d,
+                                    words_f8_d, out, stream=None):
+    import torch
+    _check(lib().tilemix_prefill_varlen3_qinline(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
+        _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(k_i8, torch.int8, "k_i8"),
+        _dptr(k_scale, torch.float32, "k_scale"), _dptr(k_f8, torch.uint8, "k_f8"),
+        _dptr(k_scale_f8, torch.float32, "k_scale_f8"), _dptr(words_i8_d, torch.int64, "words_i8_d"),
+        _dptr(words_f8_d, torch.int64, "words_f8_d"), _dptr(out, torch.float16, "out"), _stream(stream)))
 
 
 def tilemix_quantize_qk_fp8(plan_h, plan_d, q, k, q_f8, k_f8, q_scale_f8, k_scale_f8, stream=None):
@@ -456,11 +476,14 @@ class TileMixPrefill3(TileMixPrefill):
             setattr(self, name, torch.from_numpy(w.view(np.int64)).to(self.device))
 
     def quantize_k(self, k, stream=None):
-        raise TileMixError(-2, "the three-path prefill reads Q's INT8 and FP8 codes from its quantisers; "
-                               "inline Q quantisation is a two-path variant")
+        """The key halves of both quantisers (for ``attend_qinline``)."""
+        tilemix_quantize_k(self.plan_h, self.plan_d, k, self.k_i8, self.k_scale, stream)
+        tilemix_quantize_k_fp8(self.plan_h, self.plan_d, k, self.k_f8, self.k_scale_f8, stream)
 
     def attend_qinline(self, q, k, v, out, stream=None):
-        self.quantize_k(k, stream)
+        """``attend`` with Q's INT8 and FP8 codes made inside the kernel."""
+        tilemix_prefill_varlen3_qinline(self.plan_h, self.plan_d, q, k, v, self.k_i8, self.k_scale, self.k_f8,
+                                        self.k_scale_f8, self.words_d, self.words_f8_d, out, stream)
 
     def quantize(self, q, k, stream=None):
         super().quantize(q, k, stream)

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void quantize_qk_fp8_kernel(QuantFp8Args 
   __shared__ float red[4];
   const int32_t* seqtab = a.plan + kHeaderLen;
   int bid = blockIdx.x;
-  const int nq = a.tq * a.hq;
+  const int nq = a.q ? a.tq * a.hq : 0;  // no Q pointer: the key blocks only
   if (bid < nq) {
     const int tile = bid / a.hq, head = bid % a.hq;
     const int s = find_seq(seqtab, a.batch, kSeqQtOff, tile);
@@ -331,6 +331,7 @@ struct Tile {
   static constexpr int kLds = 2 * kBuf + kScales * 4;
   static constexpr int kLds3 = kLds + kScales * 4;  // + the FP8 key-tile scales
   static constexpr int kLdsQ = kLds + 16;             // + the Q absmax exchange
+  static constexpr int kLds3Q = kLds3 + 16;
 };
 
 // Combine a value with the same register of lane l ^ 32 (no LDS round trip).
@@ -484,7 +485,7 @@ __device__ inline void load_q(const _Float16* qrow, const int8_t* q8row, bool va
 // 16 kk + 8 hh + 0..7) and moved into the INT8 one (dims 32 kk + 16 hh +
 // 0..15) by one exchange per dword with lane l ^ 32.  Returns the scale.
 template <int D>
-__device__ inline float quantize_q_inline(const half8* qf, int4v* qb, float* red, int w) {
+__device__ inline float quantize_q_inline(const half8* qf, int4v* qb, float* red, int w, float* amax_out) {
   const int lane = threadIdx.x & 63;
   half2v m2[4] = {};
 #pragma unroll
@@ -501,6 +502,7 @@ __device__ inline float quantize_q_inline(const half8* qf, int4v* qb, float* red
   if (lane == 0) red[w] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  *amax_out = amax;
   const float s = __fdiv_rn(amax, 127.0f);
   const float rs = amax > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
   // Straight-line pass: t = fl(x * rs + 1.5 * 2^23) rounds the exact product
@@ -549,6 +551,73 @@ __device__ inline float quantize_q_inline(const half8* qf, int4v* qb, float* red
     const auto r0 = __builtin_amdgcn_permlane32_swap(cw[2 * kk2][0], cw[2 * kk2 + 1][0], false, false);
     const auto r1 = __builtin_amdgcn_permlane32_swap(cw[2 * kk2][1], cw[2 * kk2 + 1][1], false, false);
     qb[kk2] = (int4v){(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
+  }
+  return s;
+}
+
+// The same Q block's E4M3 codes ([Digest, method] blocks; s = fl(a / 448),
+// code = E4M3 round-half-even of fl(x / s), as the FP8 quantiser), from the
+// block absmax a.  fl(x / s) lies strictly between x * rl and x * rh, where
+// rl and rh are fl(1 / s) nudged down and up by 2^-21 (each product is then
+// within 2^-22 of x / s on its own side), and the conversion is monotone: where
+// both products give the same code, so does fl(x / s).  A wave with any other
+// element redoes its block row with the IEEE quotient.  Codes are made in the
+// fp16 fragment order and exchanged with lane l ^ 32 into the FP8 one (lane
+// half hh holds dims 64 kk + 32 hh + 0..31).  Returns the scale.
+template <int D>
+__device__ inline float quantize_q_inline_f8(const half8* qf, int8v* qc, float amax) {
+  const float s = __fdiv_rn(amax, 448.0f);
+  const float rs = amax > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  const float rl = rs * (1.0f - 0x1p-21f), rh = rs * (1.0f + 0x1p-21f);
+  uint32_t cw[D / 16][2];
+  bool split = false;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float lo[4], hi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = (float)qf[kk][4 * h + j];
+        lo[j] = x * rl;
+        hi[j] = x * rh;
+      }
+      int cl = __builtin_amdgcn_cvt_pk_fp8_f32(lo[0], lo[1], 0, false);
+      cl = __builtin_amdgcn_cvt_pk_fp8_f32(lo[2], lo[3], cl, true);
+      int ch = __builtin_amdgcn_cvt_pk_fp8_f32(hi[0], hi[1], 0, false);
+      ch = __builtin_amdgcn_cvt_pk_fp8_f32(hi[2], hi[3], ch, true);
+      split |= cl != ch;
+      cw[kk][h] = (uint32_t)cl;
+    }
+  if (__builtin_amdgcn_ballot_w64(split)) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = amax > 0.f ? __fdiv_rn((float)qf[kk][4 * h + j], s) : 0.f;
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
+        cw[kk][h] = (uint32_t)c;
+      }
+  }
+  // Group m (8 dims) of the FP8 fragment kk: the low lane half takes its own
+  // fp16 groups 4kk, 4kk+1 and the high half's same ones; the high half the
+  // low half's 4kk+2, 4kk+3 and its own.
+#pragma unroll
+  for (int kk = 0; kk < D / 64; ++kk) {
+    uint32_t g[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const auto a = __builtin_amdgcn_permlane32_swap(cw[4 * kk][h], cw[4 * kk + 2][h], false, false);
+      const auto b = __builtin_amdgcn_permlane32_swap(cw[4 * kk + 1][h], cw[4 * kk + 3][h], false, false);
+      g[0 + h] = a[0];
+      g[2 + h] = a[1];
+      g[4 + h] = b[0];
+      g[6 + h] = b[1];
+    }
+    qc[kk] = (int8v){(int)g[0], (int)g[1], (int)g[2], (int)g[3], (int)g[4], (int)g[5], (int)g[6], (int)g[7]};
   }
   return s;
 }
@@ -718,11 +787,11 @@ __device__ __forceinline__ void tile_step(const char* buf, int code, float f_i8,
 
 // kThree adds the FP8 path: a second word per (KV head, row) marks FP8
 // groups (never also INT8); without it the kernel is the two-path one.
-// kQInline (two-path only): the unit's Q block is quantised in the prologue
-// instead of read from the quantiser's output (a.qi8, a.qs unused).
+// kQInline: the unit's Q block is quantised in the prologue (INT8, and FP8
+// with kThree) instead of read from the quantisers' output (a.qi8, a.qs,
+// a.qf8, a.qsf8 unused).
 template <int D, bool kThree, bool kQInline = false>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
-  static_assert(!(kThree && kQInline), "inline Q quantisation is a two-path variant");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   using T = Tile<D>;
 
@@ -773,7 +842,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     load_q<D>(a.q + ((size_t)(start + qi) * a.hq + head) * D,
               a.qi8 + ((size_t)(start + qi) * a.hq + head) * D, qvalid, qf, qb);
   int8v qc[kThree ? D / 64 : 1];  // FP8 query codes: 32 per lane per 64-wide step
-  if (kThree) {
+  if (kThree && !kQInline) {
     const uint8_t* qrow = a.qf8 + ((size_t)(start + qi) * a.hq + head) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk) {
@@ -789,7 +858,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // asm-issued tile loads, so a wait it placed later for these would also
   // wait for every tile load in flight.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  float sq;
+  float sq, sqf = 0.f;
   if (kQInline) {
     const _Float16* qrow = a.q + ((size_t)(start + qi) * a.hq + head) * D;
 #pragma unroll
@@ -798,13 +867,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       if (qvalid) v = *reinterpret_cast<const half8*>(qrow + kk * 16 + (lane >> 5) * 8);
       qf[kk] = v;
     }
-    float* red = reinterpret_cast<float*>(smem + 2 * T::kBuf) + T::kScales;
-    const float s = quantize_q_inline<D>(qf, qb, red, w);
+    // past the key-tile scales (and the FP8 ones): those are staged below
+    // while slower waves may still read the exchanged maxima
+    float* red = reinterpret_cast<float*>(smem + 2 * T::kBuf) + (kThree ? 2 : 1) * T::kScales;
+    float amax;
+    const float s = quantize_q_inline<D>(qf, qb, red, w, &amax);
     sq = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s)));
+    if (kThree) {
+      const float sf = quantize_q_inline_f8<D>(qf, qc, amax);
+      sqf = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sf)));
+    }
   } else {
     sq = load_uniform(a.qs + (size_t)head * a.tq + qt_off + row);
+    if (kThree) sqf = load_uniform(a.qsf8 + (size_t)head * a.tq + qt_off + row);
   }
-  const float sqf = kThree ? load_uniform(a.qsf8 + (size_t)head * a.tq + qt_off + row) : 0.f;
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
   const float scale16 = inv_sqrt_d * kLog2e;
   // The row's key-tile scales go through LDS (1024 tiles per chunk): a scalar
@@ -1185,6 +1261,89 @@ int tilemix_prefill_varlen3(const int32_t* plan_h, const int32_t* plan_d, const 
     hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(grid), dim3(kThreads), Tile<128>::kLds3, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "prefill3 launch");
+  return TILEMIX_OK;
+}
+
+int tilemix_quantize_k_fp8(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, uint8_t* k_f8,
+                           float* k_scale_f8, void* hip_stream) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const bool any = plan_h[kTotalTokens] > 0;
+  if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(k_f16, "k_f16", any)) ||
+      (rc = check_dev_ptr(k_f8, "k_f8", any)) || (rc = check_dev_ptr(k_scale_f8, "k_scale_f8", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  QuantFp8Args a;
+  a.plan = plan_d;
+  a.q = nullptr;  // key blocks only
+  a.k = static_cast<const _Float16*>(k_f16);
+  a.qf8 = nullptr;
+  a.kf8 = k_f8;
+  a.qs = nullptr;
+  a.ks = k_scale_f8;
+  a.hq = plan_h[kHq];
+  a.hkv = plan_h[kHkv];
+  a.batch = plan_h[kBatch];
+  a.tq = plan_h[kTotalQTiles];
+  a.tk = plan_h[kTotalKTiles];
+  const int64_t blocks = (int64_t)a.tk * a.hkv;
+  if (blocks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (plan_h[kHeadDim] == 64)
+    hipLaunchKernelGGL(quantize_qk_fp8_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(quantize_qk_fp8_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "quantize_k_fp8 launch");
+  return TILEMIX_OK;
+}
+
+int tilemix_prefill_varlen3_qinline(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                                    const void* k_f16, const void* v_f16, const int8_t* k_i8,
+                                    const float* k_scale, const uint8_t* k_f8, const float* k_scale_f8,
+                                    const uint64_t* words_i8_d, const uint64_t* words_f8_d, void* out_f16,
+                                    void* hip_stream) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const bool any = plan_h[kNumItems] > 0;
+  if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
+      (rc = check_dev_ptr(k_f16, "k_f16", any)) || (rc = check_dev_ptr(v_f16, "v_f16", any)) ||
+      (rc = check_dev_ptr(k_i8, "k_i8", any)) || (rc = check_dev_ptr(k_scale, "k_scale", any)) ||
+      (rc = check_dev_ptr(k_f8, "k_f8", any)) || (rc = check_dev_ptr(k_scale_f8, "k_scale_f8", any)) ||
+      (rc = check_dev_ptr(words_i8_d, "words_i8_d", any)) || (rc = check_dev_ptr(words_f8_d, "words_f8_d", any)) ||
+      (rc = check_dev_ptr(out_f16, "out_f16", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  PrefillArgs a;
+  a.plan = plan_d;
+  a.q = static_cast<const _Float16*>(q_f16);
+  a.k = static_cast<const _Float16*>(k_f16);
+  a.v = static_cast<const _Float16*>(v_f16);
+  a.qi8 = nullptr;  // Q is quantised in the kernel
+  a.ki8 = k_i8;
+  a.qs = nullptr;
+  a.ks = k_scale;
+  a.words = words_i8_d;
+  a.out = static_cast<_Float16*>(out_f16);
+  a.qf8 = nullptr;
+  a.kf8 = k_f8;
+  a.qsf8 = nullptr;
+  a.ksf8 = k_scale_f8;
+  a.wordsf8 = words_f8_d;
+  a.hq = plan_h[kHq];
+  a.hkv = plan_h[kHkv];
+  a.tq = plan_h[kTotalQTiles];
+  a.tk = plan_h[kTotalKTiles];
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const unsigned grid = (unsigned)plan_h[kNumItems];
+  if (plan_h[kHeadDim] == 64)
+    hipLaunchKernelGGL((prefill_kernel<64, true, true>), dim3(grid), dim3(kThreads), Tile<64>::kLds3Q, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<128, true, true>), dim3(grid), dim3(kThreads), Tile<128>::kLds3Q, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "prefill3_qinline launch");
   return TILEMIX_OK;
 }
 

@@ -278,10 +278,19 @@ def test_stack_argument_validation():
     assert rc == -1 and "workspace" in tm.tilemix_last_error()
 
 
-def test_three_path_rejects_inline_q():
-    # the inline-Q prefill is a two-path kernel: the three-path object refuses
-    # it before touching any buffer
-    tp = tm.TileMixPrefill3.__new__(tm.TileMixPrefill3)
-    with pytest.raises(tm.TileMixError, match="two-path") as e:
-        tp(None, None, None, out=object(), inline_q=True)
-    assert e.value.code == -2
+def test_three_path_inline_entry_validation():
+    cu = synth.cu_seqlens_of([200, 70])
+    plan = tm.tilemix_build_plan(cu, 2, 1, 64)
+    lib = tm.lib()
+    p = ctypes.c_void_p(plan.ctypes.data)
+    fake = ctypes.c_void_p(16)
+    odd = ctypes.c_void_p(24)
+    assert lib.tilemix_quantize_k_fp8(p, fake, fake, fake, None, None) == -1
+    assert "k_scale_f8 is NULL" in tm.tilemix_last_error()
+    assert lib.tilemix_prefill_varlen3_qinline(p, fake, fake, fake, fake, fake, fake, odd, fake, fake, fake,
+                                               fake, None) == -1
+    assert "k_f8" in tm.tilemix_last_error() and "aligned" in tm.tilemix_last_error()
+    empty = tm.tilemix_build_plan(np.array([0, 0], dtype=np.int32), 2, 1, 64)
+    e = ctypes.c_void_p(empty.ctypes.data)
+    assert lib.tilemix_quantize_k_fp8(e, fake, None, None, None, None) == 0
+    assert lib.tilemix_prefill_varlen3_qinline(e, fake, *([None] * 10), None) == 0

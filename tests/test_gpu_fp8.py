@@ -226,3 +226,67 @@ def test_three_path_headline_sampled(c8, cf):
         err = np.abs(out[a + rows, h].astype(np.float64) - ref[a + rows, h]).max(axis=1)
         assert np.all(np.isfinite(out[a + rows, h]))
         assert np.all(err <= MAX_ABS + bound), (s, h, r, float((err - MAX_ABS - bound).max()))
+
+
+# ------------------------------------- Q's INT8 and FP8 codes made in-kernel
+
+def three_path_both(q, k, v, cu, hq, hkv, template, c8, cf, seed=0):
+    """The three-path prefill after the two Q/K quantisers, and the variant
+    that quantises Q inside the kernel after the key-only quantisers; the key
+    codes of both quantiser pairs must agree."""
+    tp, ref, _ = run3(q, k, v, cu, hq, hkv, template, c8, cf, seed)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    saved = [t.clone() for t in (tp.k_i8, tp.k_scale, tp.k_f8, tp.k_scale_f8)]
+    tp.k_i8.fill_(0x55)
+    tp.k_f8.fill_(0x55)
+    tp.k_scale.fill_(float("nan"))
+    tp.k_scale_f8.fill_(float("nan"))
+    out = torch.full_like(qd, float("nan"))
+    tp(qd, kd, vd, out, inline_q=True)
+    torch.cuda.synchronize()
+    T = q.shape[0]
+    for a, b in zip((tp.k_i8, tp.k_f8), saved[0:4:2]):
+        assert torch.equal(a[:T], b[:T])
+    for a, b in zip((tp.k_scale, tp.k_scale_f8), saved[1:4:2]):
+        assert torch.equal(a[:, :tp.tk].view(torch.int32), b[:, :tp.tk].view(torch.int32))
+    return ref, out.cpu().numpy()
+
+
+def assert_bits_equal(a, b):
+    same = a.view(np.uint16) == b.view(np.uint16)
+    assert same.all(), f"{int((~same).sum())} of {same.size} outputs differ"
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d,c8,cf", [([300, 77, 0, 129, 1, 520], 6, 2, 64, 5000, 2500),
+                                                 ([300, 77, 0, 129, 1, 520], 6, 2, 128, 0, 10000),
+                                                 ([1024, 200], 24, 8, 128, 2500, 5000)])
+def test_three_path_qinline_bit_identical(lens, hq, hkv, d, c8, cf):
+    _log(f"three-path inline-Q lens={lens} d={d} int8 {c8} fp8 {cf}")
+    q, k, v, cu = synth.make_qkv(lens, hq, hkv, d, outliers=True, seed=37)
+    ref, out = three_path_both(q, k, v, cu, hq, hkv, "sptrans", c8, cf)
+    assert_bits_equal(ref, out)
+
+
+def test_three_path_qinline_midpoints_and_zero_blocks():
+    # absmax 448 makes s = 1: values on E4M3 rounding midpoints (ties to even),
+    # an all-zero block (s = 0) and a block scaled far down
+    _log("three-path inline-Q midpoints / zero blocks")
+    lens, hq, hkv, d = [300], 3, 1, 64
+    q, k, v, cu = synth.make_qkv(lens, hq, hkv, d, outliers=False, seed=43)
+    q[:128, 0] = 0
+    q[:128, 1] = 0
+    q[:128, 1, 0] = 448.0
+    q[:128, 1, 1:9] = np.array([1.0625, -1.1875, 17.0, -19.0, 0.015625 * 1.0625, 100.0, -232.0, 3.125],
+                               dtype=np.float16)
+    q[128:256, 2] *= 1e-3
+    for c8, cf in [(0, 10000), (5000, 5000)]:
+        ref, out = three_path_both(q, k, v, cu, hq, hkv, "band", c8, cf)
+        assert_bits_equal(ref, out)
+
+
+@pytest.mark.parametrize("c8,cf", [(5000, 2500), (0, 7500)])
+def test_three_path_qinline_headline_bit_identical(c8, cf):
+    _log(f"three-path inline-Q 3B L=4096 B=8 int8 {c8} fp8 {cf}")
+    q, k, v, cu, spec = synth.make_workload("llama3b_l4k")
+    ref, out = three_path_both(q, k, v, cu, spec["hq"], spec["hkv"], "sptrans", c8, cf)
+    assert_bits_equal(ref, out)
