@@ -100,3 +100,14 @@ def test_headline_bit_identical(cov):
     q, k, v, cu, spec = synth.make_workload("llama3b_l4k")
     ref, out, _ = both_paths(q, k, v, cu, spec["hq"], spec["hkv"], "sptrans", cov)
     assert_bit_identical(ref, out)
+
+
+@pytest.mark.parametrize("workload,template,cov", [("llama3b_l8k", "rowrandom", 5000),
+                                                   ("qwen2_7b_varlen", None, None)])
+def test_other_workloads_bit_identical(workload, template, cov):
+    q, k, v, cu, spec = synth.make_workload(workload)
+    template = template or spec["template"]
+    cov = spec["coverage_bp"] if cov is None else cov
+    _log(f"qinline {workload} {template} cov={cov}")
+    ref, out, _ = both_paths(q, k, v, cu, spec["hq"], spec["hkv"], template, cov)
+    assert_bit_identical(ref, out)
