@@ -838,9 +838,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   half8 qf[D / 16];
   int4v qb[D / 32];
-  if (!kQInline)
+  if (!kQInline) {
     load_q<D>(a.q + ((size_t)(start + qi) * a.hq + head) * D,
               a.qi8 + ((size_t)(start + qi) * a.hq + head) * D, qvalid, qf, qb);
+  } else {
+    // the fp16 fragments only (quantised below), in flight with the first tile
+    const _Float16* qrow = a.q + ((size_t)(start + qi) * a.hq + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      half8 v = {};
+      if (qvalid) v = *reinterpret_cast<const half8*>(qrow + kk * 16 + (lane >> 5) * 8);
+      qf[kk] = v;
+    }
+  }
   int8v qc[kThree ? D / 64 : 1];  // FP8 query codes: 32 per lane per 64-wide step
   if (kThree && !kQInline) {
     const uint8_t* qrow = a.qf8 + ((size_t)(start + qi) * a.hq + head) * D;
@@ -860,13 +870,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   float sq, sqf = 0.f;
   if (kQInline) {
-    const _Float16* qrow = a.q + ((size_t)(start + qi) * a.hq + head) * D;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      half8 v = {};
-      if (qvalid) v = *reinterpret_cast<const half8*>(qrow + kk * 16 + (lane >> 5) * 8);
-      qf[kk] = v;
-    }
     // past the key-tile scales (and the FP8 ones): those are staged below
     // while slower waves may still read the exchanged maxima
     float* red = reinterpret_cast<float*>(smem + 2 * T::kBuf) + (kThree ? 2 : 1) * T::kScales;
