@@ -245,6 +245,12 @@ int tilemix_prefill_varlen3(const int32_t* plan_h, const int32_t* plan_d, const 
 int tilemix_quantize_k_fp8(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, uint8_t* k_f8,
                            float* k_scale_f8, void* hip_stream);
 
+/* Both key quantisers in one pass over K (device): the codes and scales of
+ * tilemix_quantize_k and tilemix_quantize_k_fp8, bit for bit, from a single
+ * read of each key block.  Outputs as those two calls. */
+int tilemix_quantize_k_i8_fp8(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, int8_t* k_i8,
+                              float* k_scale, uint8_t* k_f8, float* k_scale_f8, void* hip_stream);
+
 /* tilemix_prefill_varlen3 with Q's INT8 and FP8 codes made inside the kernel
  * (device), one Q block per work unit as in tilemix_prefill_varlen_qinline:
  * the INT8 codes with the arithmetic of tilemix_quantize_qk and the E4M3 codes

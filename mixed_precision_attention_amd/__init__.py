@@ -57,6 +57,7 @@ _SIGNATURES = {
     "tilemix_quantize_k": ([_P] * 6, ctypes.c_int),
     "tilemix_prefill_varlen_qinline": ([_P] * 10, ctypes.c_int),
     "tilemix_quantize_k_fp8": ([_P] * 6, ctypes.c_int),
+    "tilemix_quantize_k_i8_fp8": ([_P] * 8, ctypes.c_int),
     "tilemix_prefill_varlen3_qinline": ([_P] * 13, ctypes.c_int),
     "tilemix_debug_qk_i32_tile": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
     "tilemix_quantize_kv": ([_P] * 9, ctypes.c_int),
@@ -243,6 +244,14 @@ def tilemix_quantize_k_fp8(plan_h, plan_d, k, k_f8, k_scale_f8, stream=None):
     _check(lib().tilemix_quantize_k_fp8(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(k, torch.float16, "k"),
         _dptr(k_f8, torch.uint8, "k_f8"), _dptr(k_scale_f8, torch.float32, "k_scale_f8"), _stream(stream)))
+
+
+def tilemix_quantize_k_i8_fp8(plan_h, plan_d, k, k_i8, k_scale, k_f8, k_scale_f8, stream=None):
+    import torch
+    _check(lib().tilemix_quantize_k_i8_fp8(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(k, torch.float16, "k"),
+        _dptr(k_i8, torch.int8, "k_i8"), _dptr(k_scale, torch.float32, "k_scale"), _dptr(k_f8, torch.uint8, "k_f8"),
+        _dptr(k_scale_f8, torch.float32, "k_scale_f8"), _stream(stream)))
 
 
 def tilemix_prefill_varlen3_qinline(plan_h, plan_d, q, k, v, k_i8, k_scale, k_f8, k_scale_f8, words_i8_d,
@@ -476,9 +485,10 @@ class TileMixPrefill3(TileMixPrefill):
             setattr(self, name, torch.from_numpy(w.view(np.int64)).to(self.device))
 
     def quantize_k(self, k, stream=None):
-        """The key halves of both quantisers (for ``attend_qinline``)."""
-        tilemix_quantize_k(self.plan_h, self.plan_d, k, self.k_i8, self.k_scale, stream)
-        tilemix_quantize_k_fp8(self.plan_h, self.plan_d, k, self.k_f8, self.k_scale_f8, stream)
+        """The key halves of both quantisers, in one pass over K (for
+        ``attend_qinline``)."""
+        tilemix_quantize_k_i8_fp8(self.plan_h, self.plan_d, k, self.k_i8, self.k_scale, self.k_f8,
+                                  self.k_scale_f8, stream)
 
     def attend_qinline(self, q, k, v, out, stream=None):
         """``attend`` with Q's INT8 and FP8 codes made inside the kernel."""

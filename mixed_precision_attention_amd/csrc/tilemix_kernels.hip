@@ -202,6 +202,88 @@ __device__ inline void quantize_block_fp8(const _Float16* src, uint8_t* dst, flo
   }
 }
 
+// Both key codes of one block from a single read: the INT8 codes of
+// quantize_block and the E4M3 codes of quantize_block_fp8, element for
+// element the same arithmetic, from the one absmax.
+template <int D, int BLK>
+__device__ inline void quantize_block_i8_fp8(const _Float16* src, int8_t* dst8, uint8_t* dstf, float* scale8,
+                                             float* scalef, int row_stride, int nrows, float* red) {
+  constexpr int kChunksPerRow = D / 8;
+  constexpr int kPerThread = BLK * kChunksPerRow / kThreads;
+  const int tid = threadIdx.x;
+  half8 vals[kPerThread];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / kChunksPerRow, cc = idx % kChunksPerRow;
+    half8 v = {};
+    if (r < nrows) v = *reinterpret_cast<const half8*>(src + (size_t)r * row_stride + cc * 8);
+    vals[i] = v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)v[j]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s8 = __fdiv_rn(amax, 127.0f);
+  const float sf = __fdiv_rn(amax, 448.0f);
+  if (tid == 0) {
+    *scale8 = s8;
+    *scalef = sf;
+  }
+  const float rs8 = amax > 0.f ? __fdiv_rn(1.0f, s8) : 0.f;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / kChunksPerRow, cc = idx % kChunksPerRow;
+    if (r >= nrows) continue;
+    uint32_t lo = 0, hi = 0;
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t b = (uint32_t)(quant_code_i8((float)vals[i][j], rs8, s8) & 0xff);
+      if (j < 4) lo |= b << (8 * j); else hi |= b << (8 * (j - 4));
+      y[j] = amax > 0.f ? __fdiv_rn((float)vals[i][j], sf) : 0.f;
+    }
+    *reinterpret_cast<uint2*>(dst8 + (size_t)r * row_stride + cc * 8) = make_uint2(lo, hi);
+    int flo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    flo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], flo, true);
+    int fhi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    fhi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], fhi, true);
+    *reinterpret_cast<uint2*>(dstf + (size_t)r * row_stride + cc * 8) = make_uint2((uint32_t)flo, (uint32_t)fhi);
+  }
+}
+
+struct QuantKBothArgs {
+  const int32_t* plan;
+  const _Float16* k;
+  int8_t* ki8;
+  uint8_t* kf8;
+  float* ks;
+  float* ksf8;
+  int32_t hkv, batch, tk;
+};
+
+// One workgroup per (key block, KV head).
+template <int D>
+__global__ __launch_bounds__(kThreads) void quantize_k_i8_fp8_kernel(QuantKBothArgs a) {
+  __shared__ float red[4];
+  const int32_t* seqtab = a.plan + kHeaderLen;
+  const int bid = blockIdx.x;
+  const int tile = bid / a.hkv, head = bid % a.hkv;
+  const int s = find_seq(seqtab, a.batch, kSeqKtOff, tile);
+  const int32_t* rec = seqtab + s * kSeqStride;
+  const int local = tile - rec[kSeqKtOff];
+  const int row0 = rec[kSeqStart] + local * kBlockN;
+  const int nrows = min(kBlockN, rec[kSeqLen] - local * kBlockN);
+  const size_t base = ((size_t)row0 * a.hkv + head) * D;
+  quantize_block_i8_fp8<D, kBlockN>(a.k + base, a.ki8 + base, a.kf8 + base, a.ks + (size_t)head * a.tk + tile,
+                                    a.ksf8 + (size_t)head * a.tk + tile, a.hkv * D, nrows, red);
+}
+
 struct QuantFp8Args {
   const int32_t* plan;
   const _Float16* q;
@@ -1299,6 +1381,39 @@ int tilemix_quantize_k_fp8(const int32_t* plan_h, const int32_t* plan_d, const v
     hipLaunchKernelGGL(quantize_qk_fp8_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "quantize_k_fp8 launch");
+  return TILEMIX_OK;
+}
+
+int tilemix_quantize_k_i8_fp8(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, int8_t* k_i8,
+                              float* k_scale, uint8_t* k_f8, float* k_scale_f8, void* hip_stream) {
+  clear_error();
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const bool any = plan_h[kTotalTokens] > 0;
+  if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(k_f16, "k_f16", any)) ||
+      (rc = check_dev_ptr(k_i8, "k_i8", any)) || (rc = check_dev_ptr(k_scale, "k_scale", any)) ||
+      (rc = check_dev_ptr(k_f8, "k_f8", any)) || (rc = check_dev_ptr(k_scale_f8, "k_scale_f8", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  QuantKBothArgs a;
+  a.plan = plan_d;
+  a.k = static_cast<const _Float16*>(k_f16);
+  a.ki8 = k_i8;
+  a.kf8 = k_f8;
+  a.ks = k_scale;
+  a.ksf8 = k_scale_f8;
+  a.hkv = plan_h[kHkv];
+  a.batch = plan_h[kBatch];
+  a.tk = plan_h[kTotalKTiles];
+  const int64_t blocks = (int64_t)a.tk * a.hkv;
+  if (blocks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (plan_h[kHeadDim] == 64)
+    hipLaunchKernelGGL(quantize_k_i8_fp8_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(quantize_k_i8_fp8_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "quantize_k_i8_fp8 launch");
   return TILEMIX_OK;
 }
 

@@ -287,10 +287,13 @@ def test_three_path_inline_entry_validation():
     odd = ctypes.c_void_p(24)
     assert lib.tilemix_quantize_k_fp8(p, fake, fake, fake, None, None) == -1
     assert "k_scale_f8 is NULL" in tm.tilemix_last_error()
+    assert lib.tilemix_quantize_k_i8_fp8(p, fake, fake, fake, fake, odd, fake, None) == -1
+    assert "k_f8" in tm.tilemix_last_error() and "aligned" in tm.tilemix_last_error()
     assert lib.tilemix_prefill_varlen3_qinline(p, fake, fake, fake, fake, fake, fake, odd, fake, fake, fake,
                                                fake, None) == -1
     assert "k_f8" in tm.tilemix_last_error() and "aligned" in tm.tilemix_last_error()
     empty = tm.tilemix_build_plan(np.array([0, 0], dtype=np.int32), 2, 1, 64)
     e = ctypes.c_void_p(empty.ctypes.data)
     assert lib.tilemix_quantize_k_fp8(e, fake, None, None, None, None) == 0
+    assert lib.tilemix_quantize_k_i8_fp8(e, fake, None, None, None, None, None, None) == 0
     assert lib.tilemix_prefill_varlen3_qinline(e, fake, *([None] * 10), None) == 0

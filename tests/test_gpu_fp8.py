@@ -290,3 +290,23 @@ def test_three_path_qinline_headline_bit_identical(c8, cf):
     q, k, v, cu, spec = synth.make_workload("llama3b_l4k")
     ref, out = three_path_both(q, k, v, cu, spec["hq"], spec["hkv"], "sptrans", c8, cf)
     assert_bits_equal(ref, out)
+
+
+@pytest.mark.parametrize("lens,hkv,d", [([300, 77, 0, 129, 1, 64], 2, 64), ([1024, 200], 8, 128)])
+def test_key_quantisers_one_pass_bit_exact(lens, hkv, d):
+    _log(f"key INT8+FP8 one pass lens={lens} hkv={hkv} d={d}")
+    q, k, v, cu = synth.make_qkv(lens, 2 * hkv, hkv, d, outliers=True, seed=47)
+    k[:64, 0] = 0  # an all-zero block: both scales 0, codes 0
+    tp = tm.TileMixPrefill3(cu, 2 * hkv, hkv, d, "band", 5000, 2500)
+    kd = torch.from_numpy(k).cuda()
+    for t in (tp.k_i8, tp.k_f8):
+        t.fill_(0x55)
+    tp.quantize_k(kd)
+    torch.cuda.synchronize()
+    T = k.shape[0]
+    ki8, ks = oracle.quantize_blocks(k, cu, 64)
+    kf8, ksf = oracle.quantize_blocks_fp8(k, cu, 64)
+    assert np.array_equal(tp.k_i8.cpu().numpy()[:T], ki8)
+    assert np.array_equal(tp.k_f8.cpu().numpy()[:T], kf8)
+    assert np.array_equal(tp.k_scale.cpu().numpy()[:, :tp.tk].view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(tp.k_scale_f8.cpu().numpy()[:, :tp.tk].view(np.uint32), ksf.view(np.uint32))
