@@ -7,7 +7,10 @@
  * that path the library offers one decode step against an INT8 key/value
  * cache, content-dependent routing words, an FP8 (E4M3) third score path and
  * the layers of a synthetic attention stack that carries the deviation from
- * layer to layer.
+ * layer to layer.  The prefill (two- or three-path) comes in two forms with
+ * bit-identical output: reading Q's codes from the quantisers, or making them
+ * in its prologue (one work unit is exactly one Q block), which leaves only
+ * K to quantise beforehand.
  *
  * Sources (web pages about TileMix), cited by title and section:
  *   [Digest]    "TileMix: Tile-Centric Mixed-Precision Attention for LLM
