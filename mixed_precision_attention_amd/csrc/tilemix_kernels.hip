@@ -592,16 +592,16 @@ __device__ inline float quantize_q_inline(const half8* qf, int4v* qb, float* red
   // whose low byte is the low byte of t's bits; e = p - code (to 2^-25).  p
   // lies within 1.2e-5 of fl(x / s) (rs's rounding plus half an ulp of the
   // quotient), so the code equals round-half-even(fl(x / s)) unless |e| >
-  // 0.5 - 2^-16.  A wave with such an element redoes its block row with
-  // quant_code_i8, element for element.
+  // 0.5 - 2^-16.  A word of four codes with such an element in any lane is
+  // redone across the wave with quant_code_i8, element for element.
   constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
   uint32_t cw[D / 16][2];
-  float emax = 0.f;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t b[4];
+      float emax = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float x = (float)qf[kk][4 * h + j];
@@ -610,20 +610,15 @@ __device__ inline float quantize_q_inline(const half8* qf, int4v* qb, float* red
         emax = fmaxf(emax, __builtin_fabsf(e));
         b[j] = __builtin_bit_cast(uint32_t, t);
       }
-      cw[kk][h] = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
-    }
-  if (__builtin_amdgcn_ballot_w64(emax > 0.5f - 0x1p-16f)) {
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t word = 0;
+      uint32_t word = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+      if (__builtin_amdgcn_ballot_w64(emax > 0.5f - 0x1p-16f)) {
+        word = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           word |= (uint32_t)(quant_code_i8((float)qf[kk][4 * h + j], rs, s) & 0xff) << (8 * j);
-        cw[kk][h] = word;
       }
-  }
+      cw[kk][h] = word;
+    }
   // Lanes 32..63 of the first operand trade places with lanes 0..31 of the
   // second: the low half keeps its own dims 32 kk2 + 0..7 and receives the
   // high half's 8..15; the high half receives the low half's 16..23 and keeps
@@ -642,8 +637,10 @@ __device__ inline float quantize_q_inline(const half8* qf, int4v* qb, float* red
 // block absmax a.  fl(x / s) lies strictly between x * rl and x * rh, where
 // rl and rh are fl(1 / s) nudged down and up by 2^-21 (each product is then
 // within 2^-22 of x / s on its own side), and the conversion is monotone: where
-// both products give the same code, so does fl(x / s).  A wave with any other
-// element redoes its block row with the IEEE quotient.  Codes are made in the
+// both products give the same code, so does fl(x / s).  A word of four codes
+// with any other element in any lane is redone across the wave with the IEEE
+// quotient (exact E4M3 ties are common: fl(x / s) lands on a midpoint for
+// about one element in a thousand of random blocks).  Codes are made in the
 // fp16 fragment order and exchanged with lane l ^ 32 into the FP8 one (lane
 // half hh holds dims 64 kk + 32 hh + 0..31).  Returns the scale.
 template <int D>
@@ -652,7 +649,6 @@ __device__ inline float quantize_q_inline_f8(const half8* qf, int8v* qc, float a
   const float rs = amax > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
   const float rl = rs * (1.0f - 0x1p-21f), rh = rs * (1.0f + 0x1p-21f);
   uint32_t cw[D / 16][2];
-  bool split = false;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
@@ -668,22 +664,15 @@ __device__ inline float quantize_q_inline_f8(const half8* qf, int8v* qc, float a
       cl = __builtin_amdgcn_cvt_pk_fp8_f32(lo[2], lo[3], cl, true);
       int ch = __builtin_amdgcn_cvt_pk_fp8_f32(hi[0], hi[1], 0, false);
       ch = __builtin_amdgcn_cvt_pk_fp8_f32(hi[2], hi[3], ch, true);
-      split |= cl != ch;
-      cw[kk][h] = (uint32_t)cl;
-    }
-  if (__builtin_amdgcn_ballot_w64(split)) {
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      if (__builtin_amdgcn_ballot_w64(cl != ch)) {
         float y[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) y[j] = amax > 0.f ? __fdiv_rn((float)qf[kk][4 * h + j], s) : 0.f;
-        int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        c = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
-        cw[kk][h] = (uint32_t)c;
+        cl = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        cl = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], cl, true);
       }
-  }
+      cw[kk][h] = (uint32_t)cl;
+    }
   // Group m (8 dims) of the FP8 fragment kk: the low lane half takes its own
   // fp16 groups 4kk, 4kk+1 and the high half's same ones; the high half the
   // low half's 4kk+2, 4kk+3 and its own.
