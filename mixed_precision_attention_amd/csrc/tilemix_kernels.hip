@@ -362,6 +362,13 @@ __device__ inline void lds_dma16(char* lds_dst, int4v rsrc, int voffset, int sof
                : "memory", "m0");
 }
 
+// The same load into a wave-uniform LDS byte address.
+__device__ inline void lds_dma16_at(unsigned lds, int4v rsrc, int voffset, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voffset),
+               "s"(rsrc), "s"(soffset)
+               : "memory", "m0");
+}
+
 template <int kRowBytes, int kPitch>
 struct Layout {
   static constexpr int kRowsPerWin = 1024 / kRowBytes;
@@ -376,6 +383,18 @@ struct Layout {
   // (window j adds j * row stride).
   __device__ static int lane_src(int lane, int gstride) {
     return (lane / kLanesPerRow) * kWins * gstride + (lane % kLanesPerRow) * 16;
+  }
+  // A tile of 64 rows inside the sequence: this wave's windows (the windows
+  // split evenly over the four waves), addressed from the tile's LDS byte
+  // address `lds_tile` without per-window checks.
+  __device__ static void issue_full(unsigned lds_tile, const void* base, int gstride, int wave, int lane_off) {
+    static_assert(kWins % 4 == 0, "windows split evenly over the four waves");
+    const int4v rsrc = make_rsrc(base);
+#pragma unroll
+    for (int i = 0; i < kWins / 4; ++i) {
+      const int j = wave + 4 * i;
+      lds_dma16_at(lds_tile + j * kPitch, rsrc, lane_off, j * gstride);
+    }
   }
   // Issue the tile whose first row is at `base`; rows >= nvalid repeat row
   // nvalid - 1 of the same sequence (finite; those keys are masked).
@@ -898,8 +917,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   auto code_of = [&](int G) {
     return ((word >> G) & 1ull) ? 1 : (kThree && ((wordf >> G) & 1ull)) ? 2 : 0;
   };
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)LDS_PTR(char, smem));
   auto issue = [&](int t, int code, char* buf) {
     const int nvalid = min(kBlockN, L - t * kBlockN);
+    if (nvalid == kBlockN) {  // a whole tile: the lean form
+      const unsigned lb = lds0 + (unsigned)(buf - smem);
+      if (code == 1) T::K8::issue_full(lb, k8seq + (size_t)t * kBlockN * s8, s8, w, lo8);
+      else if (kThree && code == 2) T::K8::issue_full(lb, kf8seq + (size_t)t * kBlockN * s8, s8, w, lo8);
+      else T::K16::issue_full(lb, kseq + (size_t)t * kBlockN * s16, s16, w, lo16);
+      T::V::issue_full(lb + T::kKRegion, vseq + (size_t)t * kBlockN * s16, s16, w, lov);
+      return;
+    }
     if (code == 1) T::K8::issue(buf, k8seq + (size_t)t * kBlockN * s8, s8, nvalid, w, lane, lo8);
     else if (kThree && code == 2) T::K8::issue(buf, kf8seq + (size_t)t * kBlockN * s8, s8, nvalid, w, lane, lo8);
     else T::K16::issue(buf, kseq + (size_t)t * kBlockN * s16, s16, nvalid, w, lane, lo16);
