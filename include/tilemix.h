@@ -127,7 +127,7 @@ int tilemix_build_routing3(const int32_t* cu_seqlens_h, int32_t batch, int32_t n
                            int64_t* legal_groups_h);
 
 /* Adaptive routing words (host) -- [Digest, setup]: the evaluated routing is
- * static, and the interface accepts adaptive policies; [Routes, "Placement
+ * static, and the interface accepts adaptive policies; [Map, "Placement
  * can matter more than the nominal percentage"].  Given the importance of
  * every legal group (from tilemix_routing_importance, copied to the host),
  * the legal groups of each (sequence, KV head) are ordered by (importance,

@@ -1,7 +1,7 @@
 // Per-group importance for adaptive routing words (gfx950).
 //
 // [Digest, setup]: the evaluated routing is static and data-free, and the
-// interface accepts adaptive policies; [Routes, "Placement can matter more
+// interface accepts adaptive policies; [Map, "Placement can matter more
 // than the nominal percentage"]: where reduced precision lands matters more
 // than how much of it there is.  This is a cheap content statistic built
 // from what the quantiser already produced:

@@ -560,10 +560,10 @@ def decode_attention(q, k_i8, k_scale, v_i8, v_scale, words, cu_seqlens, hq: int
 # Adaptive routing words from a per-tile statistic, and the importance probe
 # ---------------------------------------------------------------------------
 #
-# [Digest, setup] and [Routes, "The A100 result should not be exported
+# [Digest, setup] and [Map, "The A100 result should not be exported
 # unchanged"]: the evaluated routing is static and data-free; the interface
 # accepts adaptive policies, which the pages leave untested.  [Explainer,
-# 数字精度混用到底靠不靠谱] / [Routes, "Placement can matter more than the nominal percentage"]:
+# 数字精度混用到底靠不靠谱] / [Map, "Placement can matter more than the nominal percentage"]:
 # the pages probe a layout by the share of high-importance attention mass
 # that lands in INT8 groups (about 8.5% for SpTrans at 25%).  Readings taken
 # here (a cheap statistic from data the quantiser already produced):

@@ -19,7 +19,8 @@ def _golden():
 
 @pytest.mark.parametrize("case", _golden()["cases"], ids=lambda c: f"{c['template']}-L{c['L']}-{c['coverage_bp']}")
 def test_worked_examples(case):
-    words, g, n8, nl = oracle.routing_words([case["L"]], 1, case["template"], case["coverage_bp"])
+    words, g, n8, nl = oracle.routing_words([case["L"]], 1, case["template"], case["coverage_bp"],
+                                            seed=case.get("seed", 0))
     assert [hex(int(w)) for w in words[0]] == case["words"]
 
 
