@@ -58,6 +58,8 @@ extern "C" {
 #define TILEMIX_BLOCK_M 128   /* query rows per score tile and per Q quant block */
 #define TILEMIX_BLOCK_N 64    /* keys per score tile and per K quant block      */
 #define TILEMIX_WORD_BITS 64  /* routing groups per query-tile row, at most     */
+/* Scratch bytes the allocation-free decode step holds per GPU (32 MiB). */
+#define TILEMIX_DECODE_SCRATCH_BYTES (32ll * 1024 * 1024)
 
 enum tilemix_status {
   TILEMIX_OK = 0,
@@ -292,6 +294,23 @@ int tilemix_decode_varlen(const int32_t* plan_h, const int32_t* plan_d, const vo
                           const int8_t* k_i8, const int8_t* v_i8, const float* k_scale,
                           const float* v_scale, const uint64_t* words_d, void* workspace,
                           int64_t workspace_bytes, void* out_f16, void* hip_stream);
+
+/* tilemix_decode_varlen without the workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The partial-softmax records live
+ * in a static device array of TILEMIX_DECODE_SCRATCH_BYTES per GPU, owned by
+ * the library and held until the process ends; its address is looked up once
+ * per device, on the first call with that device current.  Same arguments,
+ * kernels and output as tilemix_decode_varlen; nothing is allocated.  Every
+ * call on a GPU shares that GPU's array (each record is written before it is
+ * read, so nothing needs clearing between calls): calls that overlap on one
+ * GPU (other streams, other threads) race.  Errors: as tilemix_decode_varlen,
+ * plus EINVAL when tilemix_decode_workspace_size exceeds
+ * TILEMIX_DECODE_SCRATCH_BYTES (use tilemix_decode_varlen then). */
+int tilemix_decode_varlen_noalloc(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                                  const int8_t* k_i8, const int8_t* v_i8, const float* k_scale,
+                                  const float* v_scale, const uint64_t* words_d, void* out_f16,
+                                  void* hip_stream);
 
 /* Bytes of device workspace tilemix_routing_importance needs:
  * (Hq * total_q_tiles + Hkv * total_k_tiles) * d * 4. */

@@ -69,6 +69,7 @@ _SIGNATURES = {
     "tilemix_routing_importance": ([_P] * 7 + [_I64, _P, _P], ctypes.c_int),
     "tilemix_decode_workspace_size": ([_P, _P], ctypes.c_int),
     "tilemix_decode_varlen": ([_P] * 9 + [_I64, _P, _P], ctypes.c_int),
+    "tilemix_decode_varlen_noalloc": ([_P] * 10, ctypes.c_int),
     "tilemix_stack_rms_norm": ([_P, _P, _I64, _I32, _I32, _I32, ctypes.c_float, _P], ctypes.c_int),
     "tilemix_stack_qkv": ([_P] * 5 + [_I64, _I32, _I32, _I32, _P], ctypes.c_int),
     "tilemix_stack_out_residual": ([_P] * 3 + [_I64, _I32, _I32, _I32, _P], ctypes.c_int),
@@ -340,6 +341,18 @@ def tilemix_decode_varlen(plan_h, plan_d, q, k_i8, v_i8, k_scale, v_scale, words
         _stream(stream)))
 
 
+def tilemix_decode_varlen_noalloc(plan_h, plan_d, q, k_i8, v_i8, k_scale, v_scale, words_d, out,
+                                  stream=None):
+    """tilemix_decode_varlen with its scratch in the library's static device
+    array (nothing allocated; calls that overlap on one GPU race)."""
+    import torch
+    _check(lib().tilemix_decode_varlen_noalloc(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
+        _dptr(k_i8, torch.int8, "k_i8"), _dptr(v_i8, torch.int8, "v_i8"),
+        _dptr(k_scale, torch.float32, "k_scale"), _dptr(v_scale, torch.float32, "v_scale"),
+        _dptr(words_d, torch.int64, "words_d"), _dptr(out, torch.float16, "out"), _stream(stream)))
+
+
 def tilemix_stack_rms_norm(x, u, hq: int, hkv: int, head_dim: int, eps: float, stream=None):
     import torch
     _check(lib().tilemix_stack_rms_norm(
@@ -538,13 +551,19 @@ class TileMixDecode:
         tilemix_quantize_kv(self.plan_h, self.plan_d, k, v, self.k_i8, self.v_i8, self.k_scale,
                             self.v_scale, stream)
 
-    def step(self, q, out=None, stream=None):
-        """q: fp16 [B, Hq, d], the newest query of each sequence."""
+    def step(self, q, out=None, stream=None, noalloc: bool = False):
+        """q: fp16 [B, Hq, d], the newest query of each sequence.  With
+        ``noalloc`` the step keeps its partial records in the library's static
+        scratch instead of ``self.workspace`` (the same output)."""
         import torch
         if out is None:
             out = torch.empty((self.batch, self.hq, self.d), dtype=torch.float16, device=q.device)
-        tilemix_decode_varlen(self.plan_h, self.plan_d, q, self.k_i8, self.v_i8, self.k_scale,
-                              self.v_scale, self.words_d, self.workspace, out, stream)
+        if noalloc:
+            tilemix_decode_varlen_noalloc(self.plan_h, self.plan_d, q, self.k_i8, self.v_i8, self.k_scale,
+                                          self.v_scale, self.words_d, out, stream)
+        else:
+            tilemix_decode_varlen(self.plan_h, self.plan_d, q, self.k_i8, self.v_i8, self.k_scale,
+                                  self.v_scale, self.words_d, self.workspace, out, stream)
         return out
 
 

@@ -20,10 +20,17 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "tilemix.h"
 #include "tilemix_host.h"
 #include "tilemix_internal.h"
+
+// Scratch of the allocation-free decode entry point: the partial-softmax
+// records, in a static device array (one copy per GPU the library runs on,
+// held until the process ends).  Host code never passes the array's name to a
+// kernel: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[TILEMIX_DECODE_SCRATCH_BYTES];
 
 namespace tilemix {
 namespace decode {
@@ -430,6 +437,90 @@ int64_t max_chunks(const int32_t* plan_h) {
   return m;
 }
 
+constexpr int64_t kDecodeScratchBytes = TILEMIX_DECODE_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int decode_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TILEMIX_EUNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(TILEMIX_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TILEMIX_OK;
+}
+
+// The decode step's launches, with the partial records at `work`
+// (the caller checked its size).
+int decode_launch(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16, const int8_t* k_i8,
+                  const int8_t* v_i8, const float* k_scale, const float* v_scale, const uint64_t* words_d,
+                  float* work, void* out_f16, void* hip_stream) {
+  const int32_t batch = plan_h[kBatch];
+  if (batch == 0) return TILEMIX_OK;
+  DecodeArgs a;
+  a.plan = plan_d;
+  a.q = static_cast<const _Float16*>(q_f16);
+  a.ki8 = k_i8;
+  a.vi8 = v_i8;
+  a.ks = k_scale;
+  a.vs = v_scale;
+  a.words = words_d;
+  a.work = work;
+  a.out = static_cast<_Float16*>(out_f16);
+  a.batch = batch;
+  a.hq = plan_h[kHq];
+  a.hkv = plan_h[kHkv];
+  a.tq = plan_h[kTotalQTiles];
+  a.tk = plan_h[kTotalKTiles];
+  a.chunks = (int32_t)max_chunks(plan_h);
+  const int grp = a.hq / a.hkv;
+  a.head_groups = (grp + kMaxG - 1) / kMaxG;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const int64_t gy = (int64_t)batch * a.hkv * a.head_groups;
+  if (gy > 65535 || a.chunks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  const int d = plan_h[kHeadDim];
+  if (a.chunks > 0) {
+    const dim3 grid(a.chunks, (unsigned)gy);
+    const int kg = std::min(grp, kMaxG);
+    if (d == 64) launch_partial<64>(kg, grid, st, a);
+    else launch_partial<128>(kg, grid, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  const unsigned merge = (unsigned)(((int64_t)batch * a.hq + 3) / 4);  // one wave per (sequence, head)
+  if (d == 64)
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(merge), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(merge), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+  return TILEMIX_OK;
+}
+
+int decode_check(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16, const int8_t* k_i8,
+                 const int8_t* v_i8, const float* k_scale, const float* v_scale, const uint64_t* words_d,
+                 void* out_f16) {
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  const int32_t batch = plan_h[kBatch];
+  const bool any = plan_h[kTotalTokens] > 0;
+  if ((rc = check_ptr(plan_d, "plan_d", true)) || (rc = check_ptr(q_f16, "q_f16", batch > 0)) ||
+      (rc = check_ptr(k_i8, "k_i8", any)) || (rc = check_ptr(v_i8, "v_i8", any)) ||
+      (rc = check_ptr(k_scale, "k_scale", any)) || (rc = check_ptr(v_scale, "v_scale", any)) ||
+      (rc = check_ptr(words_d, "words_d", any)) || (rc = check_ptr(out_f16, "out_f16", batch > 0)))
+    return rc;
+  return TILEMIX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -485,60 +576,35 @@ int tilemix_decode_varlen(const int32_t* plan_h, const int32_t* plan_d, const vo
                           const float* v_scale, const uint64_t* words_d, void* workspace,
                           int64_t workspace_bytes, void* out_f16, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = decode_check(plan_h, plan_d, q_f16, k_i8, v_i8, k_scale, v_scale, words_d, out_f16);
   if (rc) return rc;
-  const int32_t batch = plan_h[kBatch];
-  const bool any = plan_h[kTotalTokens] > 0;
-  if ((rc = check_ptr(plan_d, "plan_d", true)) || (rc = check_ptr(q_f16, "q_f16", batch > 0)) ||
-      (rc = check_ptr(k_i8, "k_i8", any)) || (rc = check_ptr(v_i8, "v_i8", any)) ||
-      (rc = check_ptr(k_scale, "k_scale", any)) || (rc = check_ptr(v_scale, "v_scale", any)) ||
-      (rc = check_ptr(words_d, "words_d", any)) || (rc = check_ptr(workspace, "workspace", any)) ||
-      (rc = check_ptr(out_f16, "out_f16", batch > 0)))
-    return rc;
+  if ((rc = check_ptr(workspace, "workspace", plan_h[kTotalTokens] > 0))) return rc;
   int64_t need = 0;
   tilemix_decode_workspace_size(plan_h, &need);
   if (workspace_bytes < need)
     return fail(TILEMIX_EINVAL, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes,
                 (long long)need);
-  if (batch == 0) return TILEMIX_OK;
-  DecodeArgs a;
-  a.plan = plan_d;
-  a.q = static_cast<const _Float16*>(q_f16);
-  a.ki8 = k_i8;
-  a.vi8 = v_i8;
-  a.ks = k_scale;
-  a.vs = v_scale;
-  a.words = words_d;
-  a.work = static_cast<float*>(workspace);
-  a.out = static_cast<_Float16*>(out_f16);
-  a.batch = batch;
-  a.hq = plan_h[kHq];
-  a.hkv = plan_h[kHkv];
-  a.tq = plan_h[kTotalQTiles];
-  a.tk = plan_h[kTotalKTiles];
-  a.chunks = (int32_t)max_chunks(plan_h);
-  const int grp = a.hq / a.hkv;
-  a.head_groups = (grp + kMaxG - 1) / kMaxG;
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const int64_t gy = (int64_t)batch * a.hkv * a.head_groups;
-  if (gy > 65535 || a.chunks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
-  const int d = plan_h[kHeadDim];
-  if (a.chunks > 0) {
-    const dim3 grid(a.chunks, (unsigned)gy);
-    const int kg = std::min(grp, kMaxG);
-    if (d == 64) launch_partial<64>(kg, grid, st, a);
-    else launch_partial<128>(kg, grid, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-  }
-  const unsigned merge = (unsigned)(((int64_t)batch * a.hq + 3) / 4);  // one wave per (sequence, head)
-  if (d == 64)
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(merge), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(merge), dim3(kThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "decode merge launch");
-  return TILEMIX_OK;
+  return decode_launch(plan_h, plan_d, q_f16, k_i8, v_i8, k_scale, v_scale, words_d,
+                       static_cast<float*>(workspace), out_f16, hip_stream);
+}
+
+int tilemix_decode_varlen_noalloc(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
+                                  const int8_t* k_i8, const int8_t* v_i8, const float* k_scale,
+                                  const float* v_scale, const uint64_t* words_d, void* out_f16,
+                                  void* hip_stream) {
+  clear_error();
+  int rc = decode_check(plan_h, plan_d, q_f16, k_i8, v_i8, k_scale, v_scale, words_d, out_f16);
+  if (rc) return rc;
+  int64_t need = 0;
+  tilemix_decode_workspace_size(plan_h, &need);
+  if (need > kDecodeScratchBytes)
+    return fail(TILEMIX_EINVAL, "decode step needs %lld bytes of scratch, more than the %lld the "
+                "allocation-free entry point holds; use tilemix_decode_varlen with a workspace",
+                (long long)need, (long long)kDecodeScratchBytes);
+  void* work = nullptr;
+  if ((rc = decode_scratch(&work))) return rc;
+  return decode_launch(plan_h, plan_d, q_f16, k_i8, v_i8, k_scale, v_scale, words_d,
+                       static_cast<float*>(work), out_f16, hip_stream);
 }
 
 }  // extern "C"

@@ -297,3 +297,17 @@ def test_three_path_inline_entry_validation():
     assert lib.tilemix_quantize_k_fp8(e, fake, None, None, None, None) == 0
     assert lib.tilemix_quantize_k_i8_fp8(e, fake, None, None, None, None, None, None) == 0
     assert lib.tilemix_prefill_varlen3_qinline(e, fake, *([None] * 10), None) == 0
+
+
+def test_decode_noalloc_rejects_oversized_step_on_the_host():
+    """The allocation-free decode step refuses, before any HIP call, a step
+    whose partial records exceed its static scratch (fake device pointers:
+    nothing is dereferenced on that path)."""
+    lens = [65600, 1, 1, 1]
+    plan_h = tm.tilemix_build_plan(synth.cu_seqlens_of(lens), 64, 8, 128)
+    assert tm.tilemix_decode_workspace_size(plan_h) > 32 * 1024 * 1024
+    fake = ctypes.c_void_p(1 << 20)
+    rc = tm.lib().tilemix_decode_varlen_noalloc(plan_h.ctypes.data_as(ctypes.c_void_p), fake, fake, fake, fake,
+                                               fake, fake, fake, fake, None)
+    assert rc == -1
+    assert "scratch" in tm.tilemix_last_error()
