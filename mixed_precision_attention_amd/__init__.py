@@ -22,7 +22,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtilemix.so")
+# The in-tree build; TILEMIX_LIB may name one of build.py's checking builds
+# (``_build/debug`` or ``_build/host_sanitize``) instead.
+LIB_PATH = os.environ.get("TILEMIX_LIB") or os.path.join(_HERE, "libtilemix.so")
 
 BLOCK_M = 128
 BLOCK_N = 64

@@ -201,7 +201,7 @@ int tilemix_routing_importance(const int32_t* plan_h, const int32_t* plan_d, con
                                void* workspace, int64_t workspace_bytes, float* importance_d,
                                void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kTotalTokens] > 0;
   if ((rc = check_ptr(plan_d, "plan_d", true)) || (rc = check_ptr(q_i8, "q_i8", any)) ||

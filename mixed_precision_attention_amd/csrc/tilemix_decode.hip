@@ -509,7 +509,7 @@ int decode_launch(const int32_t* plan_h, const int32_t* plan_d, const void* q_f1
 int decode_check(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16, const int8_t* k_i8,
                  const int8_t* v_i8, const float* k_scale, const float* v_scale, const uint64_t* words_d,
                  void* out_f16) {
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const int32_t batch = plan_h[kBatch];
   const bool any = plan_h[kTotalTokens] > 0;
@@ -529,7 +529,7 @@ int tilemix_quantize_kv(const int32_t* plan_h, const int32_t* plan_d, const void
                         const void* v_f16, int8_t* k_i8, int8_t* v_i8, float* k_scale,
                         float* v_scale, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kTotalTokens] > 0;
   if ((rc = check_ptr(plan_d, "plan_d", true)) || (rc = check_ptr(k_f16, "k_f16", any)) ||

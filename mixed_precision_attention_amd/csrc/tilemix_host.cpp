@@ -232,12 +232,39 @@ std::vector<Group> template_order(const SeqGeo& geo, int32_t tmpl, uint64_t seed
 // ---------------------------------------------------------------------------
 // Planner
 // ---------------------------------------------------------------------------
+int64_t plan_length(const int32_t* plan_h) {
+  return kHeaderLen + (int64_t)plan_h[kBatch] * kSeqStride + (int64_t)plan_h[kNumItems] * kItemStride;
+}
+
+uint32_t plan_hash(const int32_t* plan_h) {
+  uint32_t h = 2166136261u;
+  const int64_t n = plan_length(plan_h);
+  for (int64_t i = 0; i < n; ++i) {
+    if (i == kPlanHash) continue;
+    uint32_t w = (uint32_t)plan_h[i];
+    for (int b = 0; b < 4; ++b, w >>= 8) {
+      h ^= w & 0xffu;
+      h *= 16777619u;
+    }
+  }
+  return h;
+}
+
+// The header's fields are checked for consistency before the hash reads the
+// body, so a damaged header cannot send the check past the plan's end.
 int check_plan(const int32_t* plan_h) {
   if (plan_h == nullptr) return fail(TILEMIX_EINVAL, "plan_h is NULL");
   if (plan_h[kMagic] != kPlanMagic) return fail(TILEMIX_EINVAL, "plan_h is not a TileMix plan");
   if (plan_h[kVersion] != kPlanVersion)
     return fail(TILEMIX_EUNSUPPORTED, "plan version %d, library expects %d", plan_h[kVersion],
                 kPlanVersion);
+  const int32_t batch = plan_h[kBatch];
+  if (batch < 0 || plan_h[kHq] <= 0 || plan_h[kHkv] <= 0 || plan_h[kHq] % plan_h[kHkv] != 0 ||
+      (plan_h[kHeadDim] != 64 && plan_h[kHeadDim] != 128) || plan_h[kNumItems] < 0 ||
+      plan_h[kSeqOff] != kHeaderLen || plan_h[kItemOff] != kHeaderLen + batch * kSeqStride)
+    return fail(TILEMIX_EINVAL, "plan_h header is inconsistent");
+  if ((uint32_t)plan_h[kPlanHash] != plan_hash(plan_h))
+    return fail(TILEMIX_EINVAL, "plan_h does not match its checksum (modified or truncated plan)");
   return TILEMIX_OK;
 }
 
@@ -375,8 +402,9 @@ int tilemix_build_routing(const int32_t* cu_seqlens_h, int32_t batch, int32_t nu
       const int64_t n8 = (coverage_bp * n_legal + 5000) / 10000;
       std::vector<uint64_t> w(geo.Tm, 0);
       for (int64_t i = n_legal - n8; i < n_legal; ++i) w[order[i].r] |= 1ull << order[i].G;
-      for (int32_t h = 0; h < num_kv_heads; ++h)
-        std::memcpy(words_h + h * total_tm + off, w.data(), geo.Tm * sizeof(uint64_t));
+      if (geo.Tm > 0)  // an empty sequence owns no words (and w.data() may be NULL)
+        for (int32_t h = 0; h < num_kv_heads; ++h)
+          std::memcpy(words_h + h * total_tm + off, w.data(), geo.Tm * sizeof(uint64_t));
       off += geo.Tm;
       if (g_h) g_h[s] = (int32_t)geo.g;
       if (int8_groups_h) int8_groups_h[s] = n8;
@@ -416,7 +444,7 @@ int tilemix_build_routing3(const int32_t* cu_seqlens_h, int32_t batch, int32_t n
       std::vector<uint64_t> w8(geo.Tm, 0), wf(geo.Tm, 0);
       for (int64_t i = n - n8; i < n; ++i) w8[order[i].r] |= 1ull << order[i].G;
       for (int64_t i = n - nboth; i < n - n8; ++i) wf[order[i].r] |= 1ull << order[i].G;
-      for (int32_t h = 0; h < num_kv_heads; ++h) {
+      for (int32_t h = 0; h < num_kv_heads && geo.Tm > 0; ++h) {
         std::memcpy(words_i8_h + h * total_tm + off, w8.data(), geo.Tm * sizeof(uint64_t));
         std::memcpy(words_f8_h + h * total_tm + off, wf.data(), geo.Tm * sizeof(uint64_t));
       }
@@ -468,7 +496,7 @@ int tilemix_build_routing_adaptive(const int32_t* cu_seqlens_h, int32_t batch, i
           return a.r != b.r ? a.r < b.r : a.G < b.G;
         });
         uint64_t* w = words_h + (int64_t)h * total_tm + off;
-        std::memset(w, 0, geo.Tm * sizeof(uint64_t));
+        if (geo.Tm > 0) std::memset(w, 0, geo.Tm * sizeof(uint64_t));
         for (int64_t i = 0; i < n8; ++i) w[order[i].r] |= 1ull << order[i].G;
       }
       off += geo.Tm;
@@ -544,6 +572,7 @@ int tilemix_build_plan(const int32_t* cu_seqlens_h, int32_t batch, int32_t hq, i
     plan_h[kItemOff] = (int32_t)(kHeaderLen + (int64_t)batch * kSeqStride);
     plan_h[kPlanDies] = kNumXcd;
     plan_h[kMaxTm] = (int32_t)max_tm;
+    plan_h[kPlanHash] = (int32_t)plan_hash(plan_h);
   } catch (const std::exception& e) {
     return fail(TILEMIX_EINVAL, "plan build failed: %s", e.what());
   }

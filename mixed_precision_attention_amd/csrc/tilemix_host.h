@@ -19,5 +19,13 @@ const char* last_error();
 bool aligned16(const void* p);
 int check_cu_seqlens(const int32_t* cu, int32_t batch);
 int check_plan(const int32_t* plan_h);
+// Length in int32 of a plan whose header passed check_plan.
+int64_t plan_length(const int32_t* plan_h);
+// FNV-1a (32-bit) of a plan's header (its hash field excluded) and body.
+uint32_t plan_hash(const int32_t* plan_h);
+// check_plan on the host copy, then the device copy's pointer; a build with
+// TILEMIX_DEBUG_PLAN also reads back the device copy's header and requires it
+// to equal the host copy's (hash included).
+int check_plans(const int32_t* plan_h, const int32_t* plan_d);
 
 }  // namespace tilemix

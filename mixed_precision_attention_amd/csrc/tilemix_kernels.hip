@@ -1111,13 +1111,31 @@ int check_dev_ptr(const void* p, const char* name, bool needed) {
 
 }  // namespace
 
+namespace tilemix {
+
+int check_plans(const int32_t* plan_h, const int32_t* plan_d) {
+  int rc = check_plan(plan_h);
+  if (rc) return rc;
+  if ((rc = check_dev_ptr(plan_d, "plan_d", true))) return rc;
+#ifdef TILEMIX_DEBUG_PLAN
+  int32_t head[kHeaderLen];
+  hipError_t e = hipMemcpy(head, plan_d, sizeof head, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading back plan_d");
+  for (int i = 0; i < kHeaderLen; ++i)
+    if (head[i] != plan_h[i]) return fail(TILEMIX_EINVAL, "plan_d is not the device copy of plan_h (field %d)", i);
+#endif
+  return TILEMIX_OK;
+}
+
+}  // namespace tilemix
+
 extern "C" {
 
 int tilemix_quantize_qk(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
                         const void* k_f16, int8_t* q_i8, int8_t* k_i8, float* q_scale,
                         float* k_scale, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kTotalTokens] > 0;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
@@ -1156,7 +1174,7 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
                            const int8_t* k_i8, const float* q_scale, const float* k_scale,
                            const uint64_t* words_d, void* out_f16, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kNumItems] > 0;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
@@ -1200,7 +1218,7 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
 int tilemix_quantize_k(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, int8_t* k_i8,
                        float* k_scale, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kTotalTokens] > 0;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(k_f16, "k_f16", any)) ||
@@ -1237,7 +1255,7 @@ int tilemix_prefill_varlen_qinline(const int32_t* plan_h, const int32_t* plan_d,
                                    const float* k_scale, const uint64_t* words_d, void* out_f16,
                                    void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kNumItems] > 0;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
@@ -1281,7 +1299,7 @@ int tilemix_quantize_qk_fp8(const int32_t* plan_h, const int32_t* plan_d, const 
                             const void* k_f16, uint8_t* q_f8, uint8_t* k_f8, float* q_scale_f8,
                             float* k_scale_f8, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kTotalTokens] > 0;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
@@ -1322,7 +1340,7 @@ int tilemix_prefill_varlen3(const int32_t* plan_h, const int32_t* plan_d, const 
                             const uint64_t* words_i8_d, const uint64_t* words_f8_d, void* out_f16,
                             void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kNumItems] > 0;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
@@ -1369,7 +1387,7 @@ int tilemix_prefill_varlen3(const int32_t* plan_h, const int32_t* plan_d, const 
 int tilemix_quantize_k_fp8(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, uint8_t* k_f8,
                            float* k_scale_f8, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kTotalTokens] > 0;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(k_f16, "k_f16", any)) ||
@@ -1404,7 +1422,7 @@ int tilemix_quantize_k_fp8(const int32_t* plan_h, const int32_t* plan_d, const v
 int tilemix_quantize_k_i8_fp8(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, int8_t* k_i8,
                               float* k_scale, uint8_t* k_f8, float* k_scale_f8, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kTotalTokens] > 0;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(k_f16, "k_f16", any)) ||
@@ -1440,7 +1458,7 @@ int tilemix_prefill_varlen3_qinline(const int32_t* plan_h, const int32_t* plan_d
                                     const uint64_t* words_i8_d, const uint64_t* words_f8_d, void* out_f16,
                                     void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const bool any = plan_h[kNumItems] > 0;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_f16, "q_f16", any)) ||
@@ -1486,7 +1504,7 @@ int tilemix_debug_qk_i32_tile(const int32_t* plan_h, const int32_t* plan_d, cons
                               const int8_t* k_i8, int32_t seq, int32_t head, int32_t r, int32_t t,
                               int32_t* acc_d, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   if ((rc = check_dev_ptr(plan_d, "plan_d", true)) || (rc = check_dev_ptr(q_i8, "q_i8", true)) ||
       (rc = check_dev_ptr(k_i8, "k_i8", true)) || (rc = check_dev_ptr(acc_d, "acc_d", true)))

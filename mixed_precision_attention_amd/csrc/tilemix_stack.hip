@@ -451,7 +451,7 @@ int tilemix_stack_layer(const int32_t* plan_h, const int32_t* plan_d, const uint
                         const void* wqkv_f16, const void* wo_f16, float eps, void* workspace,
                         int64_t workspace_bytes, void* hip_stream) {
   clear_error();
-  int rc = check_plan(plan_h);
+  int rc = check_plans(plan_h, plan_d);
   if (rc) return rc;
   const int64_t T = plan_h[kTotalTokens];
   const int32_t hq = plan_h[kHq], hkv = plan_h[kHkv], d = plan_h[kHeadDim];
