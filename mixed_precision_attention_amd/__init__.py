@@ -123,6 +123,30 @@ def _dptr(t, dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _dims(plan_h):
+    """(T, B, Hq, Hkv, d, total_q_tiles, total_k_tiles) from a plan's header."""
+    p = np.asarray(plan_h)
+    if p.dtype != np.int32 or p.ndim != 1 or p.size < 16:
+        raise TileMixError(-1, "plan_h must be the int32 array tilemix_build_plan returned")
+    return int(p[6]), int(p[2]), int(p[3]), int(p[4]), int(p[5]), int(p[7]), int(p[8])
+
+
+def _sizes(plan_h, plan_d=None, **need):
+    """Refuse, before any launch, a tensor smaller than the plan makes the
+    kernels touch (name=(tensor, elements)), and a device plan that is not
+    plan_h's size."""
+    if plan_d is not None and plan_d.numel() != np.asarray(plan_h).size:
+        raise TileMixError(-1, f"plan_d holds {plan_d.numel()} int32, plan_h {np.asarray(plan_h).size}: "
+                               "plan_d must be the device copy of plan_h")
+    for name, (t, n) in need.items():
+        if t is None:
+            if n > 0:
+                raise TileMixError(-1, f"{name} is missing")
+            continue
+        if t.numel() < n:
+            raise TileMixError(-1, f"{name} holds {t.numel()} elements; the plan needs {n}")
+
+
 def _stream(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -208,6 +232,9 @@ def tilemix_build_plan(cu_seqlens, hq: int, hkv: int, head_dim: int) -> np.ndarr
 
 def tilemix_quantize_qk(plan_h, plan_d, q, k, q_i8, k_i8, q_scale, k_scale, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q=(q, T * hq * d), k=(k, T * hkv * d), q_i8=(q_i8, T * hq * d), k_i8=(k_i8, T * hkv * d),
+           q_scale=(q_scale, hq * tq), k_scale=(k_scale, hkv * tk))
     _check(lib().tilemix_quantize_qk(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
         _dptr(k, torch.float16, "k"), _dptr(q_i8, torch.int8, "q_i8"), _dptr(k_i8, torch.int8, "k_i8"),
@@ -218,6 +245,10 @@ def tilemix_quantize_qk(plan_h, plan_d, q, k, q_i8, k_i8, q_scale, k_scale, stre
 def tilemix_prefill_varlen(plan_h, plan_d, q, k, v, q_i8, k_i8, q_scale, k_scale, words_d, out,
                            stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q=(q, T * hq * d), k=(k, T * hkv * d), v=(v, T * hkv * d), q_i8=(q_i8, T * hq * d),
+           k_i8=(k_i8, T * hkv * d), q_scale=(q_scale, hq * tq), k_scale=(k_scale, hkv * tk),
+           words_d=(words_d, hkv * tq), out=(out, T * hq * d))
     _check(lib().tilemix_prefill_varlen(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
         _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(q_i8, torch.int8, "q_i8"),
@@ -228,6 +259,8 @@ def tilemix_prefill_varlen(plan_h, plan_d, q, k, v, q_i8, k_i8, q_scale, k_scale
 
 def tilemix_quantize_k(plan_h, plan_d, k, k_i8, k_scale, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, k=(k, T * hkv * d), k_i8=(k_i8, T * hkv * d), k_scale=(k_scale, hkv * tk))
     _check(lib().tilemix_quantize_k(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(k, torch.float16, "k"),
         _dptr(k_i8, torch.int8, "k_i8"), _dptr(k_scale, torch.float32, "k_scale"), _stream(stream)))
@@ -235,6 +268,9 @@ def tilemix_quantize_k(plan_h, plan_d, k, k_i8, k_scale, stream=None):
 
 def tilemix_prefill_varlen_qinline(plan_h, plan_d, q, k, v, k_i8, k_scale, words_d, out, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q=(q, T * hq * d), k=(k, T * hkv * d), v=(v, T * hkv * d), k_i8=(k_i8, T * hkv * d),
+           k_scale=(k_scale, hkv * tk), words_d=(words_d, hkv * tq), out=(out, T * hq * d))
     _check(lib().tilemix_prefill_varlen_qinline(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
         _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(k_i8, torch.int8, "k_i8"),
@@ -244,6 +280,8 @@ def tilemix_prefill_varlen_qinline(plan_h, plan_d, q, k, v, k_i8, k_scale, words
 
 def tilemix_quantize_k_fp8(plan_h, plan_d, k, k_f8, k_scale_f8, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, k=(k, T * hkv * d), k_f8=(k_f8, T * hkv * d), k_scale_f8=(k_scale_f8, hkv * tk))
     _check(lib().tilemix_quantize_k_fp8(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(k, torch.float16, "k"),
         _dptr(k_f8, torch.uint8, "k_f8"), _dptr(k_scale_f8, torch.float32, "k_scale_f8"), _stream(stream)))
@@ -251,6 +289,9 @@ def tilemix_quantize_k_fp8(plan_h, plan_d, k, k_f8, k_scale_f8, stream=None):
 
 def tilemix_quantize_k_i8_fp8(plan_h, plan_d, k, k_i8, k_scale, k_f8, k_scale_f8, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, k=(k, T * hkv * d), k_i8=(k_i8, T * hkv * d), k_scale=(k_scale, hkv * tk),
+           k_f8=(k_f8, T * hkv * d), k_scale_f8=(k_scale_f8, hkv * tk))
     _check(lib().tilemix_quantize_k_i8_fp8(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(k, torch.float16, "k"),
         _dptr(k_i8, torch.int8, "k_i8"), _dptr(k_scale, torch.float32, "k_scale"), _dptr(k_f8, torch.uint8, "k_f8"),
@@ -260,6 +301,10 @@ def tilemix_quantize_k_i8_fp8(plan_h, plan_d, k, k_i8, k_scale, k_f8, k_scale_f8
 def tilemix_prefill_varlen3_qinline(plan_h, plan_d, q, k, v, k_i8, k_scale, k_f8, k_scale_f8, words_i8_d,
                                     words_f8_d, out, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q=(q, T * hq * d), k=(k, T * hkv * d), v=(v, T * hkv * d), k_i8=(k_i8, T * hkv * d),
+           k_scale=(k_scale, hkv * tk), k_f8=(k_f8, T * hkv * d), k_scale_f8=(k_scale_f8, hkv * tk),
+           words_i8_d=(words_i8_d, hkv * tq), words_f8_d=(words_f8_d, hkv * tq), out=(out, T * hq * d))
     _check(lib().tilemix_prefill_varlen3_qinline(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
         _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(k_i8, torch.int8, "k_i8"),
@@ -270,6 +315,9 @@ def tilemix_prefill_varlen3_qinline(plan_h, plan_d, q, k, v, k_i8, k_scale, k_f8
 
 def tilemix_quantize_qk_fp8(plan_h, plan_d, q, k, q_f8, k_f8, q_scale_f8, k_scale_f8, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q=(q, T * hq * d), k=(k, T * hkv * d), q_f8=(q_f8, T * hq * d), k_f8=(k_f8, T * hkv * d),
+           q_scale_f8=(q_scale_f8, hq * tq), k_scale_f8=(k_scale_f8, hkv * tk))
     _check(lib().tilemix_quantize_qk_fp8(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
         _dptr(k, torch.float16, "k"), _dptr(q_f8, torch.uint8, "q_f8"), _dptr(k_f8, torch.uint8, "k_f8"),
@@ -280,6 +328,12 @@ def tilemix_quantize_qk_fp8(plan_h, plan_d, q, k, q_f8, k_f8, q_scale_f8, k_scal
 def tilemix_prefill_varlen3(plan_h, plan_d, q, k, v, q_i8, k_i8, q_scale, k_scale, q_f8, k_f8, q_scale_f8,
                             k_scale_f8, words_i8_d, words_f8_d, out, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q=(q, T * hq * d), k=(k, T * hkv * d), v=(v, T * hkv * d), q_i8=(q_i8, T * hq * d),
+           k_i8=(k_i8, T * hkv * d), q_scale=(q_scale, hq * tq), k_scale=(k_scale, hkv * tk),
+           q_f8=(q_f8, T * hq * d), k_f8=(k_f8, T * hkv * d), q_scale_f8=(q_scale_f8, hq * tq),
+           k_scale_f8=(k_scale_f8, hkv * tk), words_i8_d=(words_i8_d, hkv * tq), words_f8_d=(words_f8_d, hkv * tq),
+           out=(out, T * hq * d))
     _check(lib().tilemix_prefill_varlen3(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
         _dptr(k, torch.float16, "k"), _dptr(v, torch.float16, "v"), _dptr(q_i8, torch.int8, "q_i8"),
@@ -293,6 +347,8 @@ def tilemix_prefill_varlen3(plan_h, plan_d, q, k, v, q_i8, k_i8, q_scale, k_scal
 def tilemix_debug_qk_i32_tile(plan_h, plan_d, q_i8, k_i8, seq: int, head: int, r: int, t: int,
                               acc, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q_i8=(q_i8, T * hq * d), k_i8=(k_i8, T * hkv * d), acc=(acc, 128 * 64))
     _check(lib().tilemix_debug_qk_i32_tile(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q_i8, torch.int8, "q_i8"),
         _dptr(k_i8, torch.int8, "k_i8"), seq, head, r, t, _dptr(acc, torch.int32, "acc"),
@@ -308,6 +364,9 @@ def tilemix_importance_workspace_size(plan_h) -> int:
 def tilemix_routing_importance(plan_h, plan_d, q_i8, k_i8, q_scale, k_scale, workspace, importance,
                                stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q_i8=(q_i8, T * hq * d), k_i8=(k_i8, T * hkv * d), q_scale=(q_scale, hq * tq),
+           k_scale=(k_scale, hkv * tk), importance=(importance, hkv * tq * 64))
     _check(lib().tilemix_routing_importance(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q_i8, torch.int8, "q_i8"),
         _dptr(k_i8, torch.int8, "k_i8"), _dptr(q_scale, torch.float32, "q_scale"),
@@ -318,6 +377,9 @@ def tilemix_routing_importance(plan_h, plan_d, q_i8, k_i8, q_scale, k_scale, wor
 
 def tilemix_quantize_kv(plan_h, plan_d, k, v, k_i8, v_i8, k_scale, v_scale, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, k=(k, T * hkv * d), v=(v, T * hkv * d), k_i8=(k_i8, T * hkv * d),
+           v_i8=(v_i8, T * hkv * d), k_scale=(k_scale, hkv * tk), v_scale=(v_scale, hkv * tk))
     _check(lib().tilemix_quantize_kv(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(k, torch.float16, "k"),
         _dptr(v, torch.float16, "v"), _dptr(k_i8, torch.int8, "k_i8"), _dptr(v_i8, torch.int8, "v_i8"),
@@ -334,6 +396,10 @@ def tilemix_decode_workspace_size(plan_h) -> int:
 def tilemix_decode_varlen(plan_h, plan_d, q, k_i8, v_i8, k_scale, v_scale, words_d, workspace, out,
                           stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q=(q, B * hq * d), k_i8=(k_i8, T * hkv * d), v_i8=(v_i8, T * hkv * d),
+           k_scale=(k_scale, hkv * tk), v_scale=(v_scale, hkv * tk), words_d=(words_d, hkv * tq),
+           out=(out, B * hq * d))
     _check(lib().tilemix_decode_varlen(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
         _dptr(k_i8, torch.int8, "k_i8"), _dptr(v_i8, torch.int8, "v_i8"),
@@ -348,6 +414,10 @@ def tilemix_decode_varlen_noalloc(plan_h, plan_d, q, k_i8, v_i8, k_scale, v_scal
     """tilemix_decode_varlen with its scratch in the library's static device
     array (nothing allocated; calls that overlap on one GPU race)."""
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q=(q, B * hq * d), k_i8=(k_i8, T * hkv * d), v_i8=(v_i8, T * hkv * d),
+           k_scale=(k_scale, hkv * tk), v_scale=(v_scale, hkv * tk), words_d=(words_d, hkv * tq),
+           out=(out, B * hq * d))
     _check(lib().tilemix_decode_varlen_noalloc(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q, torch.float16, "q"),
         _dptr(k_i8, torch.int8, "k_i8"), _dptr(v_i8, torch.int8, "v_i8"),
@@ -385,6 +455,10 @@ def tilemix_stack_workspace_size(plan_h) -> int:
 
 def tilemix_stack_layer(plan_h, plan_d, words_d, x, wqkv, wo, eps: float, workspace, stream=None):
     import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    W = (hq // hkv) * d
+    _sizes(plan_h, plan_d, words_d=(words_d, hkv * tq), x=(x, T * hq * d),
+           wqkv=(wqkv, hkv * (W + 2 * d) * W), wo=(wo, hkv * W * W))
     _check(lib().tilemix_stack_layer(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(words_d, torch.int64, "words_d"),
         _dptr(x, torch.float32, "x"), _dptr(wqkv, torch.float16, "wqkv"), _dptr(wo, torch.float16, "wo"),

@@ -311,3 +311,53 @@ def test_decode_noalloc_rejects_oversized_step_on_the_host():
                                                fake, fake, fake, fake, None)
     assert rc == -1
     assert "scratch" in tm.tilemix_last_error()
+
+
+def test_binding_refuses_tensors_smaller_than_the_plan():
+    """The binding checks every tensor against the plan before any launch (CPU
+    tensors: a wrong size is reported before the device check), and a device
+    plan whose length differs from plan_h's."""
+    torch = pytest.importorskip("torch")
+    cu = synth.cu_seqlens_of([300, 77])
+    plan = tm.tilemix_build_plan(cu, 6, 2, 64)
+    T, hq, hkv, d = 377, 6, 2, 64
+    _, tq, tk = tm.tilemix_query_sizes(cu)
+    f16 = lambda *s: torch.zeros(*s, dtype=torch.float16)
+    i8 = lambda *s: torch.zeros(*s, dtype=torch.int8)
+    f32 = lambda *s: torch.zeros(*s, dtype=torch.float32)
+    plan_d = torch.from_numpy(plan)
+    words = torch.zeros(hkv * tq, dtype=torch.int64)
+    good = dict(q=f16(T, hq, d), k=f16(T, hkv, d), v=f16(T, hkv, d), k_i8=i8(T, hkv, d), k_scale=f32(hkv, tk),
+                out=f16(T, hq, d))
+
+    def call(**over):
+        a = dict(good, **over)
+        tm.tilemix_prefill_varlen_qinline(plan, plan_d, a["q"], a["k"], a["v"], a["k_i8"], a["k_scale"],
+                                          words, a["out"])
+
+    for name, bad in (("q", f16(T - 1, hq, d)), ("k", f16(T, hkv - 1, d)), ("v", f16(T, hkv, d - 8)),
+                      ("k_i8", i8(T, hkv, d - 1)), ("k_scale", f32(hkv, tk - 1)), ("out", f16(T, hq - 1, d))):
+        with pytest.raises(tm.TileMixError, match=name + " holds"):
+            call(**{name: bad})
+    with pytest.raises(tm.TileMixError, match="device tensor"):   # right sizes: next the device check
+        call()
+    with pytest.raises(tm.TileMixError, match="plan_d"):
+        tm.tilemix_quantize_k(plan, plan_d[:-1], good["k"], good["k_i8"], good["k_scale"])
+    with pytest.raises(tm.TileMixError, match="q holds"):          # decode queries are [B, Hq, d]
+        tm.tilemix_decode_varlen(plan, plan_d, f16(1, hq, d), good["k_i8"], good["k_i8"], good["k_scale"],
+                                 good["k_scale"], words, torch.zeros(16, dtype=torch.uint8), f16(2, hq, d))
+
+
+def test_plan_checksum_refuses_a_modified_host_plan():
+    cu = synth.cu_seqlens_of([4096] * 2)
+    plan = tm.tilemix_build_plan(cu, 6, 2, 128)
+    assert plan[14] != 0
+    bad = plan.copy()
+    bad[-1] ^= 1                      # one work unit's row changed
+    fake = ctypes.c_void_p(1 << 20)
+    rc = tm.lib().tilemix_quantize_k(bad.ctypes.data_as(ctypes.c_void_p), fake, fake, fake, fake, None)
+    assert rc == -1 and "checksum" in tm.tilemix_last_error()
+    bad = plan.copy()
+    bad[9] -= 1                       # work-unit count no longer matches the body
+    rc = tm.lib().tilemix_quantize_k(bad.ctypes.data_as(ctypes.c_void_p), fake, fake, fake, fake, None)
+    assert rc == -1
