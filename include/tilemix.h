@@ -151,13 +151,28 @@ int tilemix_build_routing_adaptive(const int32_t* cu_seqlens_h, int32_t batch, i
  * caller keeps a host copy and uploads an identical device copy (both are
  * passed to the device entry points).  It depends only on (cu_seqlens, Hq,
  * Hkv, head_dim) and can be reused across layers and calls.
- * tilemix_plan_size returns its length in int32 elements in *plan_len. */
+ * tilemix_plan_size returns its length in int32 elements in *plan_len.
+ *
+ * The plan is how the device entry points receive the problem statement of
+ * [Digest, method]: cu_seqlens (host and device), the batch size, Hq, Hkv,
+ * head_dim and each sequence's grouping factor g are all in it, in place of
+ * separate arguments (the caller-owned planner workspace of the interface).
+ * plan_d must hold exactly plan_h's int32 values: the kernels read work
+ * units and sequence records from plan_d while the grid comes from plan_h.
+ * Every entry point verifies plan_h's checksum (a modified or truncated host
+ * plan is refused with EINVAL); plan_d against plan_h is verified only in the
+ * debug build (python -m mixed_precision_attention_amd.build --debug), since
+ * reading it back costs a synchronous copy -- otherwise it is the caller's
+ * duty, which the Python binding's bundles meet by uploading plan_d from
+ * plan_h themselves. */
 int tilemix_plan_size(const int32_t* cu_seqlens_h, int32_t batch, int32_t hq, int32_t hkv,
                       int32_t head_dim, int64_t* plan_len);
 int tilemix_build_plan(const int32_t* cu_seqlens_h, int32_t batch, int32_t hq, int32_t hkv,
                        int32_t head_dim, int32_t* plan_h, int64_t plan_len);
 
-/* Blockwise symmetric quantiser (device) -- [Digest, method]: only Q and K are
+/* Blockwise symmetric quantiser (device) -- [Digest, method]: the problem
+ * statement's cu_seqlens, batch, Hq, Hkv and head_dim come in through
+ * plan_h / plan_d (see the work plan above).  Only Q and K are
  * quantised, in blocks of 128 x d (Q) and 64 x d (K), symmetric with scale =
  * absmax / 127.  Per (head, block): a = max|x|, s = a / 127 and q =
  * round-half-even(x / s) clamped to [-127, 127], both divisions IEEE binary32;
@@ -171,8 +186,11 @@ int tilemix_quantize_qk(const int32_t* plan_h, const int32_t* plan_d, const void
                         float* k_scale, void* hip_stream);
 
 /* Fused mixed-precision causal prefill (device) -- [Digest, method]; [Routes,
- * precision routing]; [Map, hot loop].  For every legal key tile t of query
- * tile row r, bit = (word >> (t / g)) & 1 selects the score path:
+ * precision routing]; [Map, hot loop].  cu_seqlens, batch, Hq, Hkv, head_dim
+ * and the grouping factors g come in through plan_h / plan_d (the work plan
+ * above); words_d is the routing words' device copy.  For every legal key
+ * tile t of query tile row r, bit = (word >> (t / g)) & 1 selects the score
+ * path:
  *   bit 1: S = float(int32 sum of q_i8 * k_i8) * (s_q * s_k / sqrt(d))
  *   bit 0: S = (fp16 Q . fp16 K, fp32 accumulation) / sqrt(d)
  * then the causal / sequence-end mask (independent of the bit), one shared
