@@ -408,6 +408,17 @@ int tilemix_debug_qk_i32_tile(const int32_t* plan_h, const int32_t* plan_d, cons
                               const int8_t* k_i8, int32_t seq, int32_t head, int32_t r,
                               int32_t t, int32_t* acc_d, void* hip_stream);
 
+/* Test hook (device): the fp32 accumulator of one 128 x 64 FP8 (E4M3) score
+ * tile -- the sum over d of q_f8 * k_f8 products of E4M3 values, no scale
+ * applied -- computed by the routine the three-path kernel uses for FP8
+ * groups (the open FP8 question of [Digest, setup]; [Explainer, 写在后面]), so
+ * the accumulation of the FP8 matrix instruction can be compared with exact
+ * sums.  q_f8/k_f8 from tilemix_quantize_qk_fp8.  Entries whose query or key
+ * lies outside the sequence are 0.  acc_d: device float[128][64]. */
+int tilemix_debug_qk_f8_tile(const int32_t* plan_h, const int32_t* plan_d, const uint8_t* q_f8,
+                             const uint8_t* k_f8, int32_t seq, int32_t head, int32_t r, int32_t t,
+                             float* acc_d, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

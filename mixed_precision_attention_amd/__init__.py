@@ -62,6 +62,7 @@ _SIGNATURES = {
     "tilemix_quantize_k_i8_fp8": ([_P] * 8, ctypes.c_int),
     "tilemix_prefill_varlen3_qinline": ([_P] * 13, ctypes.c_int),
     "tilemix_debug_qk_i32_tile": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
+    "tilemix_debug_qk_f8_tile": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
     "tilemix_quantize_kv": ([_P] * 9, ctypes.c_int),
     "tilemix_build_routing3": ([_P, _I32, _I32, _I32, _I32, _I32, _U64, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "tilemix_quantize_qk_fp8": ([_P] * 9, ctypes.c_int),
@@ -352,6 +353,17 @@ def tilemix_debug_qk_i32_tile(plan_h, plan_d, q_i8, k_i8, seq: int, head: int, r
     _check(lib().tilemix_debug_qk_i32_tile(
         _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q_i8, torch.int8, "q_i8"),
         _dptr(k_i8, torch.int8, "k_i8"), seq, head, r, t, _dptr(acc, torch.int32, "acc"),
+        _stream(stream)))
+
+
+def tilemix_debug_qk_f8_tile(plan_h, plan_d, q_f8, k_f8, seq: int, head: int, r: int, t: int, acc,
+                             stream=None):
+    import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, q_f8=(q_f8, T * hq * d), k_f8=(k_f8, T * hkv * d), acc=(acc, 128 * 64))
+    _check(lib().tilemix_debug_qk_f8_tile(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(q_f8, torch.uint8, "q_f8"),
+        _dptr(k_f8, torch.uint8, "k_f8"), seq, head, r, t, _dptr(acc, torch.float32, "acc"),
         _stream(stream)))
 
 

@@ -1092,6 +1092,50 @@ __global__ __launch_bounds__(kThreads) void debug_qk_i32_kernel(const int32_t* p
     }
 }
 
+// Fp32 accumulator of one FP8 score tile (the E4M3 codes' products summed by
+// the matrix instruction, no scale applied), through the kernel's own tile
+// loader and qk_tile_f8 routine.
+template <int D>
+__global__ __launch_bounds__(kThreads) void debug_qk_f8_kernel(const int32_t* plan, const uint8_t* qf8,
+                                                               const uint8_t* kf8, int seq, int head, int row,
+                                                               int t, float* acc_out) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char sK[T::K8::kBytes];
+  const int hq = plan[kHq], hkv = plan[kHkv];
+  const int32_t* rec = plan + kHeaderLen + seq * kSeqStride;
+  const int start = rec[kSeqStart], L = rec[kSeqLen];
+  const int kv = head / (hq / hkv);
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qi = row * kBlockM + 32 * w + c;
+  const int k0 = t * kBlockN;
+  const int nvalid = min(kBlockN, L - k0);
+  const int s8 = hkv * D;
+  T::K8::issue(sK, kf8 + ((size_t)(start + k0) * hkv + kv) * D, s8, nvalid, w, lane, T::K8::lane_src(lane, s8));
+  int8v qc[D / 64];
+#pragma unroll
+  for (int kk = 0; kk < D / 64; ++kk) {
+    int4v lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+    if (qi < L) {
+      const uint8_t* qrow = qf8 + ((size_t)(start + qi) * hq + head) * D + kk * 64 + hh * 32;
+      lo = *reinterpret_cast<const int4v*>(qrow);
+      hi = *reinterpret_cast<const int4v*>(qrow + 16);
+    }
+    qc[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  wait_tile_loads();
+  __syncthreads();
+  float16v acc[2];
+  qk_tile_f8<D>(sK, qc, acc);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+      acc_out[(32 * w + c) * kBlockN + key] = (k0 + key < L && qi < L) ? acc[kb][i] : 0.f;
+    }
+}
+
 }  // namespace tilemix
 
 using namespace tilemix;
@@ -1523,6 +1567,32 @@ int tilemix_debug_qk_i32_tile(const int32_t* plan_h, const int32_t* plan_d, cons
                        seq, head, r, t, acc_d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "debug tile launch");
+  return TILEMIX_OK;
+}
+
+int tilemix_debug_qk_f8_tile(const int32_t* plan_h, const int32_t* plan_d, const uint8_t* q_f8,
+                             const uint8_t* k_f8, int32_t seq, int32_t head, int32_t r, int32_t t,
+                             float* acc_d, void* hip_stream) {
+  clear_error();
+  int rc = check_plans(plan_h, plan_d);
+  if (rc) return rc;
+  if ((rc = check_dev_ptr(q_f8, "q_f8", true)) || (rc = check_dev_ptr(k_f8, "k_f8", true)) ||
+      (rc = check_dev_ptr(acc_d, "acc_d", true)))
+    return rc;
+  if (seq < 0 || seq >= plan_h[kBatch]) return fail(TILEMIX_EINVAL, "seq %d out of range", seq);
+  if (head < 0 || head >= plan_h[kHq]) return fail(TILEMIX_EINVAL, "head %d out of range", head);
+  const int32_t* rec = plan_h + kHeaderLen + seq * kSeqStride;
+  if (r < 0 || r >= rec[kSeqTm]) return fail(TILEMIX_EINVAL, "row %d out of range", r);
+  if (t < 0 || t >= rec[kSeqTn]) return fail(TILEMIX_EINVAL, "key tile %d out of range", t);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (plan_h[kHeadDim] == 64)
+    hipLaunchKernelGGL(debug_qk_f8_kernel<64>, dim3(1), dim3(kThreads), 0, st, plan_d, q_f8, k_f8, seq, head, r,
+                       t, acc_d);
+  else
+    hipLaunchKernelGGL(debug_qk_f8_kernel<128>, dim3(1), dim3(kThreads), 0, st, plan_d, q_f8, k_f8, seq, head,
+                       r, t, acc_d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "debug fp8 tile launch");
   return TILEMIX_OK;
 }
 

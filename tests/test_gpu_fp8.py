@@ -55,13 +55,19 @@ def assert_close(got, ref):
 
 
 # The FP8 matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4) sums each
-# 64-product step with about 12 bits relative to the step's largest product
-# (measured: at most 2^-11.5 of it, for products spanning the whole E4M3
-# range), not to fp32.  On an FP8 tile the score error is therefore bounded
-# by EPS * sum over steps of max |q8 k8| * s_q s_k / sqrt(d), with EPS =
-# 2^-10.5 (twice the largest measured); a row's softmax output moves by at
-# most exp(2 delta) - 1 times max |V| for a score error delta.
-EPS_F8 = 2.0 ** -10.5
+# 64-product step with about 12 bits relative to the step's largest product,
+# not to fp32: test_fp8_tile_accumulation_bound holds every sum of a score
+# tile within EPS_F8 * (sum over steps of the step's largest |q8 k8|) of the
+# exact one (worst seen 2^-11.12, codes spanning the whole E4M3 range).  The
+# score error of an FP8 tile is then at most delta = EPS_F8 * that sum *
+# s_q s_k / sqrt(d), and a row's softmax output moves by at most
+# exp(2 delta) - 1 times max |V|.  On inputs whose blocks are dominated by a
+# few large products (the outlier channels) this lets a few rows exceed the
+# fp16 bar: those tests hold each row to 4e-3 plus that bound, all outputs
+# to F8_MAX_FACTOR times the bar (worst seen 3.6 times) and the mean to the
+# bar itself.
+EPS_F8 = 2.0 ** -11
+F8_MAX_FACTOR = 4.0
 
 
 def fp8_row_bound(q, k, v, cu, hq, hkv, tp, rows_sel):
@@ -106,9 +112,80 @@ def fp8_row_bound(q, k, v, cu, hq, hkv, tp, rows_sel):
 def assert_close_f8(got, ref, bound):
     got = got.astype(np.float64)
     assert np.all(np.isfinite(got))
-    err = np.abs(got - ref).max(axis=2)
-    excess = err - (MAX_ABS + bound)
+    err = np.abs(got - ref)
+    row = err.max(axis=2)
+    _log(f"  err max {err.max():.3e} ({err.max() / MAX_ABS:.2f} x bar), mean {err.mean():.3e}, "
+         f"rows above 4e-3 {np.mean(row > MAX_ABS):.4f}")
+    excess = row - (MAX_ABS + bound)
     assert excess.max() <= 0, f"max abs err {err.max():.3e}, worst excess {excess.max():.3e}"
+    assert err.max() <= F8_MAX_FACTOR * MAX_ABS, f"max abs err {err.max():.3e}"
+    assert err.mean() <= MEAN_ABS, f"mean abs err {err.mean():.3e}"
+
+
+def _tile_sums(codes_q, codes_k, L, d):
+    """(device sums, exact sums, per-sum bound base) of every legal FP8 score
+    tile of one single-head sequence, through the kernel's tile routine."""
+    cu = synth.cu_seqlens_of([L])
+    plan = tm.tilemix_build_plan(cu, 1, 1, d)
+    pd = torch.from_numpy(plan).cuda()
+    qd, kd = torch.from_numpy(codes_q).cuda(), torch.from_numpy(codes_k).cuda()
+    acc = torch.zeros(128 * 64, dtype=torch.float32, device="cuda")
+    qv = oracle.fp8_e4m3_decode(codes_q)[:, 0].astype(np.float64)
+    kv = oracle.fp8_e4m3_decode(codes_k)[:, 0].astype(np.float64)
+    got, exact, base = [], [], []
+    for r in range(-(-L // 128)):
+        for t in range(min(2 * r + 2, -(-L // 64))):
+            tm.tilemix_debug_qk_f8_tile(plan, pd, qd, kd, 0, 0, r, t, acc)
+            g = acc.cpu().numpy().reshape(128, 64)
+            qs, ks = np.arange(128 * r, min(128 * r + 128, L)), np.arange(64 * t, min(64 * t + 64, L))
+            prod = qv[qs][:, None, :] * kv[ks][None, :, :]
+            got.append(g[:len(qs), :len(ks)].ravel())
+            exact.append(prod.sum(axis=2).ravel())
+            base.append(np.abs(prod).reshape(len(qs), len(ks), -1, 64).max(axis=3).sum(axis=2).ravel())
+            # rows and keys past the sequence end are reported as 0
+            assert not g[len(qs):].any() and not g[:, len(ks):].any()
+    return np.concatenate(got), np.concatenate(exact), np.concatenate(base)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_tile_accumulation_bound(d):
+    """Pins EPS_F8: each sum of the FP8 score-tile routine is within EPS_F8
+    times the sum over its 64-wide steps of the step's largest |product| of
+    the exact sum of E4M3 products -- on codes spanning every finite E4M3
+    value, on quantised N(0,1) blocks, on blocks with outlier channels, and
+    on one large product among small ones; products of small exact values
+    come out exactly."""
+    L = 300
+    rng = np.random.default_rng(71)
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[np.isfinite(oracle.fp8_e4m3_decode(codes))]
+    x = rng.standard_normal((L, 1, d)).astype(np.float16)
+    y = rng.standard_normal((L, 1, d)).astype(np.float16)
+    cu = synth.cu_seqlens_of([L])
+    xo, yo = x.copy(), y.copy()
+    xo[..., :4] *= 10
+    yo[..., :4] *= 10
+    big_q = np.full((L, 1, d), 0x30, np.uint8)                    # 0.5
+    small = finite[np.abs(oracle.fp8_e4m3_decode(finite)) < 4]
+    big_k = rng.choice(small, (L, 1, d))
+    big_q[..., 5] = 0x7E                                            # 448 x 448 in step 0
+    big_k[..., 5] = 0x7E
+    cases = {
+        "every E4M3 value": (rng.choice(finite, (L, 1, d)), rng.choice(finite, (L, 1, d))),
+        "N(0,1) blocks": (oracle.quantize_blocks_fp8(x, cu, 128)[0], oracle.quantize_blocks_fp8(y, cu, 64)[0]),
+        "outlier channels": (oracle.quantize_blocks_fp8(xo, cu, 128)[0], oracle.quantize_blocks_fp8(yo, cu, 64)[0]),
+        "one large product": (big_q, big_k),
+    }
+    for name, (cq, ck) in cases.items():
+        got, exact, base = _tile_sums(cq, ck, L, d)
+        ratio = np.abs(got - exact) / np.maximum(base, 1e-300)
+        _log(f"  fp8 tile d={d} {name}: worst error / step-max sum = 2^{np.log2(max(ratio.max(), 1e-30)):.2f}")
+        assert np.all(np.abs(got - exact) <= EPS_F8 * base), name
+    # integers 1..4 times 2^-2 .. 2^1: every partial sum is exact in any format
+    # with 12 bits below the largest product, so the sums are exact
+    vals = finite[np.isin(oracle.fp8_e4m3_decode(finite), [0.25, 0.5, 1.0, 2.0, -0.5, -1.0])]
+    got, exact, _ = _tile_sums(rng.choice(vals, (L, 1, d)), rng.choice(vals, (L, 1, d)), L, d)
+    assert np.array_equal(got, exact)
 
 
 @pytest.mark.parametrize("lens,hq,hkv,d", [([256], 1, 1, 64), ([300, 77, 0, 129, 1, 64], 4, 2, 64),
@@ -204,6 +281,7 @@ def test_three_path_headline_sampled(c8, cf):
                                     rows=units)
     qv, kv_ = oracle.fp8_e4m3_decode(qf), oracle.fp8_e4m3_decode(kf)
     grp = hq // hkv
+    all_err = []
     for (s, h, r) in units:
         L, a = lens[s], int(cu[s])
         kvh = h // grp
@@ -223,9 +301,15 @@ def test_three_path_headline_sampled(c8, cf):
             delta = np.maximum(delta, EPS_F8 * steps.max(axis=1) * scale / np.sqrt(d))
         vmax = np.maximum.accumulate(np.abs(v[a:a + L, kvh].astype(np.float64)).max(axis=1))[rows]
         bound = (np.exp(2 * delta) - 1) * vmax
-        err = np.abs(out[a + rows, h].astype(np.float64) - ref[a + rows, h]).max(axis=1)
+        errs = np.abs(out[a + rows, h].astype(np.float64) - ref[a + rows, h])
+        err = errs.max(axis=1)
         assert np.all(np.isfinite(out[a + rows, h]))
         assert np.all(err <= MAX_ABS + bound), (s, h, r, float((err - MAX_ABS - bound).max()))
+        all_err.append(errs.ravel())
+    all_err = np.concatenate(all_err)
+    _log(f"  err max {all_err.max():.3e} ({all_err.max() / MAX_ABS:.2f} x bar), mean {all_err.mean():.3e}")
+    assert all_err.max() <= F8_MAX_FACTOR * MAX_ABS
+    assert all_err.mean() <= MEAN_ABS
 
 
 # ------------------------------------- Q's INT8 and FP8 codes made in-kernel
