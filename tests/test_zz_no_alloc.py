@@ -50,10 +50,11 @@ def test_noalloc_rejects_oversized_step():
     lens = [65600, 1, 1, 1]
     plan_h = tm.tilemix_build_plan(synth.cu_seqlens_of(lens), 64, 8, 128)
     assert tm.tilemix_decode_workspace_size(plan_h) > 32 * 1024 * 1024
-    dummy = torch.zeros(16, dtype=torch.float16, device="cuda")
-    i8 = torch.zeros(16, dtype=torch.int8, device="cuda")
-    f32 = torch.zeros(16, dtype=torch.float32, device="cuda")
-    words = torch.zeros(2, dtype=torch.int64, device="cuda")
+    T, (_, tq, tk) = int(synth.cu_seqlens_of(lens)[-1]), tm.tilemix_query_sizes(synth.cu_seqlens_of(lens))
+    q = torch.zeros((len(lens), 64, 128), dtype=torch.float16, device="cuda")
+    i8 = torch.zeros((T, 8, 128), dtype=torch.int8, device="cuda")
+    f32 = torch.zeros((8, tk), dtype=torch.float32, device="cuda")
+    words = torch.zeros((8, tq), dtype=torch.int64, device="cuda")
     plan_d = torch.from_numpy(plan_h).cuda()
     with pytest.raises(tm.TileMixError, match="scratch"):
-        tm.tilemix_decode_varlen_noalloc(plan_h, plan_d, dummy, i8, i8, f32, f32, words, dummy)
+        tm.tilemix_decode_varlen_noalloc(plan_h, plan_d, q, i8, i8, f32, f32, words, torch.empty_like(q))
