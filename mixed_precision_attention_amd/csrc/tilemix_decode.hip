@@ -167,7 +167,7 @@ __device__ inline void i8x4_to_half(uint32_t w, half2v& lo, half2v& hi) {
 // fewer than kMaxG of them (kG = kMaxG: a runtime count, the last group of a
 // larger set may be partial).
 template <int D, int kG>
-__global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kernel(DecodeArgs a) {
   __shared__ Smem<D> sm;
   const int chunk = blockIdx.x;
   const int hg = blockIdx.y % a.head_groups;
@@ -182,45 +182,49 @@ __global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
 
-  // Every load of the workgroup is issued up front -- the queries first, then
-  // this lane's key row and this thread's share of the staged values -- so
-  // their latencies overlap.
+  // Every load of the workgroup is issued up front, branch-free (addresses of
+  // keys past the sequence end are clamped to its last key: their scores are
+  // masked and their P is 0), in the order of first use -- the scalars, the
+  // queries, this lane's key row, then this thread's share of the values --
+  // so the waits before the scores and before P.V each cover only what they
+  // need, and the values stream in while the scores are computed.
   const int t = chunk * 4 + w;              // this wave's key tile (sequence-local)
   const int j = t * kBlockN + lane;         // this lane's key
   const bool live = j < L;
   const bool tile_live = t * kBlockN < L;
+  constexpr int kGroups = D / 4, kParts = kThreads / kGroups, kKeys = kChunk / kParts;
+  const int c4 = tid % kGroups, part = tid / kGroups;
+  const int vt = chunk * 4 + part * kKeys / kBlockN;  // key tile of this part
+  const int kt_off = rec[kSeqKtOff];
+  const float s_vp_raw = a.vs[(size_t)kv * a.tk + kt_off + min(vt, (L - 1) / kBlockN)];
+  const float s_k_raw = a.ks[(size_t)kv * a.tk + kt_off + min(t, (L - 1) / kBlockN)];
+  const uint64_t word = a.words[(size_t)kv * a.tq + rec[kSeqQtOff] + (L - 1) / kBlockM];
   _Float16 qv[2][D / 64];                   // heads w and w + 4 of the group
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int i = 0; i < D / 64; ++i)
-      qv[u][i] = w + 4 * u < G ? a.q[((size_t)seq * a.hq + h0 + w + 4 * u) * D + lane + 64 * i]
-                               : (_Float16)0.0f;
-  uint32_t kw[D / 4] = {};
-  if (live) {
-    const int4v* krow = reinterpret_cast<const int4v*>(a.ki8 + ((size_t)(start + j) * a.hkv + kv) * D);
+      qv[u][i] = a.q[((size_t)seq * a.hq + h0 + min(w + 4 * u, G - 1)) * D + lane + 64 * i];
+  uint32_t kw[D / 4];
+  {
+    const int4v* krow = reinterpret_cast<const int4v*>(a.ki8 + ((size_t)(start + min(j, L - 1)) * a.hkv + kv) * D);
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       const int4v x = krow[i];
       kw[4 * i] = x[0]; kw[4 * i + 1] = x[1]; kw[4 * i + 2] = x[2]; kw[4 * i + 3] = x[3];
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the key loads ahead of the value loads
   // Values in the P.V layout: thread (4 channels c4, key part) holds its 4
   // channels of each of its keys (a wave reads whole 128-byte rows).
-  constexpr int kGroups = D / 4, kParts = kThreads / kGroups, kKeys = kChunk / kParts;
-  const int c4 = tid % kGroups, part = tid / kGroups;
   uint32_t vreg[kKeys];
 #pragma unroll
   for (int k = 0; k < kKeys; ++k) {
-    const int jj = chunk * kChunk + part * kKeys + k;
-    vreg[k] = jj < L ? *reinterpret_cast<const uint32_t*>(a.vi8 + ((size_t)(start + jj) * a.hkv + kv) * D + c4 * 4)
-                     : 0u;
+    const int jj = min(chunk * kChunk + part * kKeys + k, L - 1);
+    vreg[k] = *reinterpret_cast<const uint32_t*>(a.vi8 + ((size_t)(start + jj) * a.hkv + kv) * D + c4 * 4);
   }
-  const int vt = chunk * 4 + part * kKeys / kBlockN;  // key tile of this part
-  const float s_vp = vt * kBlockN < L ? a.vs[(size_t)kv * a.tk + rec[kSeqKtOff] + vt] : 0.f;
-  const int kt = rec[kSeqKtOff] + t;
-  const float s_k = tile_live ? a.ks[(size_t)kv * a.tk + kt] : 0.f;
-  const uint64_t word = a.words[(size_t)kv * a.tq + rec[kSeqQtOff] + (L - 1) / kBlockM];
+  const float s_vp = vt * kBlockN < L ? s_vp_raw : 0.f;
+  const float s_k = tile_live ? s_k_raw : 0.f;
   const bool bit = tile_live && ((word >> (t / rec[kSeqG])) & 1ull);
 
   // Queries of the group: fp16 copy, and the int8 copy with one scale per
@@ -370,24 +374,53 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
   }
   const int n = (L + kChunk - 1) / kChunk;
   const float* base = a.work + ((size_t)seq * a.hq + h) * a.chunks * (D + 2);
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, base[(size_t)i * (D + 2)]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float l = 0.f;
-  for (int i = lane; i < n; i += 64) {
-    const float* r = base + (size_t)i * (D + 2);
-    l += __builtin_amdgcn_exp2f(r[0] - M) * r[1];
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+  // One pass over batches of 16 chunks: a batch's (m, l) and O rows are
+  // requested together (none depends on the others) and the next batch is
+  // requested before this one is folded in, so the merge waits about one
+  // memory latency in all.  Earlier batches' (M, l, O) are rescaled as in the
+  // online softmax.
+  float M = -INFINITY, l = 0.f;
   float acc[D / 64] = {};
-#pragma unroll 16
-  for (int i = 0; i < n; ++i) {
-    const float* r = base + (size_t)i * (D + 2);
-    const float wgt = __builtin_amdgcn_exp2f(r[0] - M);
+  float2 ml, mln;
+  float ov[16][D / 64], ovn[16][D / 64];
+  auto fetch = [&](int i0, float2& m2, float (&dst)[16][D / 64]) {
+    const int nb = min(16, n - i0);
+    m2 = lane < nb ? *reinterpret_cast<const float2*>(base + (size_t)(i0 + lane) * (D + 2))
+                   : make_float2(-INFINITY, 0.f);
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) acc[c] += wgt * r[2 + lane + 64 * c];
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c)
+        dst[i][c] = i < nb ? base[(size_t)(i0 + i) * (D + 2) + 2 + lane + 64 * c] : 0.f;
+  };
+  fetch(0, mln, ovn);
+  for (int i0 = 0; i0 < n; i0 += 16) {
+    ml = mln;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) ov[i][c] = ovn[i][c];
+    if (i0 + 16 < n) fetch(i0 + 16, mln, ovn);
+    const int nb = min(16, n - i0);
+    float mb = ml.x;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
+    const float Mn = fmaxf(M, mb);
+    const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    const float wl = lane < nb ? __builtin_amdgcn_exp2f(ml.x - Mn) : 0.f;
+    float lb = wl * ml.y;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lb += __shfl_xor(lb, off);
+    l = l * alpha + lb;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) acc[c] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float wi = __shfl(wl, i);
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) acc[c] += wi * ov[i][c];
+    }
+    M = Mn;
   }
   const float inv = 1.0f / l;
 #pragma unroll
