@@ -218,6 +218,61 @@ def bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, steps):
             "int8_pair_share": P8 / P}
 
 
+def bench_exposure(coverages=(2500, 5000, 7500), tau=0.5):
+    """Importance exposure of the SpTrans template and of the adaptive words
+    ([Explainer, 第二步] importance): per query row, the fewest keys holding a
+    share tau of the exact causal softmax's mass are its high-importance keys;
+    the figure is their mass inside INT8 groups over their whole mass, summed
+    over rows and heads.  On synthetic inputs with locality and a sink (one
+    2048-token sequence, 2 query heads over 1 KV head); routing words from the
+    library (the adaptive ones from its device importance statistic),
+    probabilities in float64 with torch on the GPU."""
+    import math
+    import numpy as np
+    import torch
+    import mixed_precision_attention_amd as tm
+    import synth
+    lens, hq, hkv, d = [2048], 2, 1, 128
+    q, k, v, cu = synth.make_qkv_local(lens, hq, hkv, d, seed=7)
+    qd, kd = (torch.from_numpy(x).cuda() for x in (q, k))
+    L = lens[0]
+    tp = tm.TileMixPrefill(cu, hq, hkv, d, "sptrans", coverages[0])
+    tp.quantize(qd, kd)
+    causal = torch.ones(L, L, dtype=torch.bool, device="cuda").triu(1)
+    probs = []
+    for h in range(hq):
+        kv = h // (hq // hkv)
+        S = (qd[:, h, :].double() @ kd[:, kv, :].double().T) / math.sqrt(d)
+        P = torch.softmax(S.masked_fill(causal, float("-inf")), dim=1)
+        sp, idx = torch.sort(P, dim=1, descending=True, stable=True)
+        cum = torch.cumsum(sp, dim=1)
+        n = (cum < tau).sum(dim=1, keepdim=True) + 1
+        sel = torch.arange(L, device="cuda")[None, :] < n
+        probs.append((kv, sp, idx, sel))
+    g = int(np.asarray(tp.g).ravel()[0])
+    rows = torch.arange(L, device="cuda") // 128
+
+    def exposure(words):
+        w = torch.from_numpy(np.ascontiguousarray(words).view(np.int64)).cuda()
+        inside = total = 0.0
+        for kv, sp, idx, sel in probs:
+            grp = (idx // 64) // g
+            bits = (w[kv, rows][:, None] >> grp) & 1
+            m = sp * sel
+            inside += float((m * bits).sum())
+            total += float(m.sum())
+        return inside / total
+
+    out = {"workload": "one 2048-token sequence with locality and a sink, hq 2, hkv 1, d 128", "tau": tau,
+           "sptrans": {}, "adaptive": {}}
+    for cov in coverages:
+        tp.set_routing("sptrans", cov)
+        out["sptrans"][str(cov)] = round(exposure(tp.words), 4)
+        tp.set_routing_adaptive(cov)
+        out["adaptive"][str(cov)] = round(exposure(tp.words), 4)
+    return out
+
+
 def bench_fp8(qd, kd, vd, cu, hq, hkv, d, template, mixes, steps):
     """Three-path prefill (FP16 / FP8 / INT8 groups) at the given (INT8, FP8)
     coverages against the three-precision MFMA roofline (FP8 at the published
@@ -435,8 +490,9 @@ def decode_bytes(cu, hq, hkv, d, tq, tk):
     tokens = int(lens.sum())
     chunks = int(sum(-(-int(L) // 256) for L in lens))
     B = len(lens)
+    # `chunks` already sums over the sequences: one record per (chunk, head)
     return (2 * tokens * hkv * d + 2 * hkv * tk * 4 + hkv * tq * 8 + 2 * B * hq * d * 2
-            + 2 * B * hq * chunks * (d + 2) * 4)
+            + 2 * hq * chunks * (d + 2) * 4)
 
 
 def bench_decode(q, k, v, cu, spec, template, coverage, steps, warmup, cpu):
@@ -526,6 +582,24 @@ def bench_decode(q, k, v, cu, spec, template, coverage, steps, warmup, cpu):
     return rec
 
 
+def _cpu_info():
+    """CPUs this process may run on, and the host CPU model."""
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cpus = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return cpus, model
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -534,7 +608,7 @@ def _blas_threads():
         return 1
 
 
-def cpu_baseline(q, k, v, cu, spec, template, coverage, budget_s=20.0):
+def cpu_baseline(q, k, v, cu, spec, template, coverage, budget_s=20.0, full_headline=False):
     """The oracle, as it stands, on a bounded sample of the workload: the
     full quantiser pass plus sampled work units of the attention,
     extrapolated to the whole batch by legal-pair count."""
@@ -576,7 +650,16 @@ def cpu_baseline(q, k, v, cu, spec, template, coverage, budget_s=20.0):
         oracle.run(qs_, ks_, vs_, cs_, sp["hq"], sp["hkv"], sp["template"], sp["coverage_bp"])
         dt = time.perf_counter() - t1
         full[name] = {"seconds": round(dt, 3), "tokens_per_s": int(cs_[-1]) / dt}
-    return {"value": tokens / t_total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    if full_headline:
+        # the headline workload's whole oracle, unsampled (minutes of CPU time)
+        t1 = time.perf_counter()
+        oracle.run(q, k, v, cu, spec["hq"], spec["hkv"], template, coverage)
+        dt = time.perf_counter() - t1
+        full[spec.get("name", "headline")] = {"seconds": round(dt, 3), "tokens_per_s": tokens / dt}
+    cpus, model = _cpu_info()
+    # numpy's BLAS pool runs the oracle's matrix products; the rest is one thread
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": int(min(threads, cpus)), "kind": "oracle",
+            "cpus_available": cpus, "cpu_model": model, "blas_threads": int(threads),
             "sample": (f"routing + full quantiser pass ({t_prep:.1f}s) + {len(done)} of {len(units)} "
                        f"(sequence, head, query-tile) units of attention ({t_attn:.1f}s, "
                        f"{pairs / total_pairs:.2%} of legal pairs), extrapolated by legal-pair count"),
@@ -606,6 +689,10 @@ def main(argv=None):
                     help="skip the synthetic multi-layer stack (deviation by depth)")
     ap.add_argument("--depth-layers", type=int, default=32)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the headline workload's whole oracle, unsampled (minutes of CPU time)")
+    ap.add_argument("--no-exposure", action="store_true",
+                    help="skip the importance-exposure probe of the SpTrans and adaptive layouts")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -749,17 +836,20 @@ def main(argv=None):
         result["sweep"] = bench_sweep(args.sweep_workload, SWEEP_TEMPLATES, SWEEP_COVERAGES)
     if not args.no_depth:
         result["depth"] = bench_depth(cu, hq, hkv, d, template, [2500, coverage], args.depth_layers)
+    if not args.no_exposure:
+        result["exposure_probe"] = bench_exposure()
     if not args.no_decode:
         spec_named = dict(spec, name=args.workload)
         result["decode"] = bench_decode(q, k, v, cu, spec_named, template, coverage, args.decode_steps,
                                         20, not args.no_cpu_baseline)
-    if any(k in result for k in ("fp8", "adaptive", "sweep", "depth", "decode")):
+    if any(k in result for k in ("fp8", "adaptive", "sweep", "depth", "decode", "exposure_probe")):
         # the headline kernel again, after the legs' seconds of sustained load
         tp.set_routing(template, coverage)  # the adaptive leg leaves its own words
         result["breakdown"]["prefill_ms_after_legs"] = time_in_pipeline(
             lambda: tp.quantize_k(kd), lambda: tp.attend_qinline(qd, kd, vd, out), K)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(q, k, v, cu, spec, template, coverage, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(q, k, v, cu, dict(spec, name=args.workload), template, coverage,
+                                              args.cpu_budget, args.cpu_full)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

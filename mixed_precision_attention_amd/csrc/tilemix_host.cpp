@@ -237,17 +237,24 @@ int64_t plan_length(const int32_t* plan_h) {
 }
 
 uint32_t plan_hash(const int32_t* plan_h) {
-  uint32_t h = 2166136261u;
+  // Four interleaved FNV-1a streams over 32-bit words (word i feeds stream
+  // i mod 4, the hash field counts as 0), folded together at the end: the
+  // multiply chains are a quarter as long as one byte-wise stream, so a plan
+  // of tens of kilobytes is checked in a few microseconds on every call.
+  constexpr uint32_t kPrime = 16777619u;
+  uint32_t h[4] = {2166136261u, 2166136261u ^ 1u, 2166136261u ^ 2u, 2166136261u ^ 3u};
   const int64_t n = plan_length(plan_h);
-  for (int64_t i = 0; i < n; ++i) {
-    if (i == kPlanHash) continue;
-    uint32_t w = (uint32_t)plan_h[i];
-    for (int b = 0; b < 4; ++b, w >>= 8) {
-      h ^= w & 0xffu;
-      h *= 16777619u;
+  int64_t i = 0;
+  for (; i + 4 <= n; i += 4)
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = (i + j == kPlanHash) ? 0u : (uint32_t)plan_h[i + j];
+      h[j] = (h[j] ^ w) * kPrime;
     }
-  }
-  return h;
+  for (int j = 0; i < n; ++i, ++j) h[j] = (h[j] ^ (i == kPlanHash ? 0u : (uint32_t)plan_h[i])) * kPrime;
+  uint32_t r = 2166136261u;
+  for (int j = 0; j < 4; ++j)
+    for (int b = 0; b < 4; ++b) r = (r ^ ((h[j] >> (8 * b)) & 0xffu)) * kPrime;
+  return r ^ (uint32_t)n;
 }
 
 // The header's fields are checked for consistency before the hash reads the

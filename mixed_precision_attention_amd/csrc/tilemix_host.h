@@ -21,7 +21,8 @@ int check_cu_seqlens(const int32_t* cu, int32_t batch);
 int check_plan(const int32_t* plan_h);
 // Length in int32 of a plan whose header passed check_plan.
 int64_t plan_length(const int32_t* plan_h);
-// FNV-1a (32-bit) of a plan's header (its hash field excluded) and body.
+// Checksum of a plan's header (its hash field counted as 0) and body: four
+// interleaved word-wise FNV-1a (32-bit) streams, folded, xor the length.
 uint32_t plan_hash(const int32_t* plan_h);
 // check_plan on the host copy, then the device copy's pointer; a build with
 // TILEMIX_DEBUG_PLAN also reads back the device copy's header and requires it

@@ -7,7 +7,7 @@
 namespace tilemix {
 
 constexpr int32_t kPlanMagic = 0x544D5850;  // "TMXP"
-constexpr int32_t kPlanVersion = 2;
+constexpr int32_t kPlanVersion = 3;
 
 // Header fields (int32 indices into the plan).
 enum PlanField : int {
@@ -25,7 +25,7 @@ enum PlanField : int {
   kItemOff = 11,      // offset of the work-unit list
   kPlanDies = 12,     // dies the list is interleaved over
   kMaxTm = 13,        // largest Tm of any sequence
-  kPlanHash = 14,     // FNV-1a (32-bit) of every other field and of the body
+  kPlanHash = 14,     // checksum (FNV-1a over words, 4 streams) of every other field and the body
   kHeaderLen = 16
 };
 
