@@ -126,9 +126,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(KvQuantArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// Partial step: one workgroup per (256-key chunk, sequence, KV head, group of
-// up to 8 query heads).  Wave w scores key tile 4 c + w, one key per lane;
-// the chunk's softmax state (m, l, unnormalised O) goes to the workspace.
+// Partial step: one workgroup per (KV head and group of up to 8 query heads,
+// 256-key chunk, sequence), the KV head fastest in the launch order so that
+// workgroups running side by side read neighbouring bytes of the same cache
+// rows.  Wave w scores key tile 4 c + w; the chunk's softmax state (m, l,
+// unnormalised O) goes to the workspace.
 // --------------------------------------------------------------------------
 struct DecodeArgs {
   const int32_t* plan;
@@ -154,6 +156,44 @@ struct Smem {
   float part[4][kMaxG][D];                          // per-wave P.V sums
 };
 
+// Lane exchanges within groups of 8 (or 4) lanes for the score reduction:
+// the partner's bit b of the lane index is the opposite of this lane's.
+template <int kMask>
+__device__ inline int xchg(int x) {
+  if constexpr (kMask == 1) return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  else if constexpr (kMask == 2) return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  else return __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror: lane ^ 7
+}
+template <int kMask>
+__device__ inline float xchg(float x) { return __builtin_bit_cast(float, xchg<kMask>(__builtin_bit_cast(int, x))); }
+
+// Sums n = kLanes partial values across the kLanes lanes that share a key
+// row and leaves lane (index mod kLanes = i) with the full sum of value i:
+// at each step a lane keeps the half of its values that its bit selects and
+// adds the partner's copy of that half (recursive halving).
+template <int kLanes, typename T>
+__device__ inline T transpose_reduce(T (&v)[kLanes], int lane) {
+  if constexpr (kLanes == 8) {
+    const bool b = lane & 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const T send = b ? v[k] : v[k + 4];
+      v[k] = (b ? v[k + 4] : v[k]) + xchg<4>(send);
+    }
+  }
+  {
+    const bool b = lane & 2;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const T send = b ? v[k] : v[k + 2];
+      v[k] = (b ? v[k + 2] : v[k]) + xchg<2>(send);
+    }
+  }
+  const bool b = lane & 1;
+  const T send = b ? v[0] : v[1];
+  return (b ? v[1] : v[0]) + xchg<1>(send);
+}
+
 // Signed int8 x4 -> two fp16 pairs, exactly: bytes b + 128 become the low
 // mantissa byte of 1024 + (b + 128) and the bias 1152 is subtracted.
 __device__ inline void i8x4_to_half(uint32_t w, half2v& lo, half2v& hi) {
@@ -169,10 +209,8 @@ __device__ inline void i8x4_to_half(uint32_t w, half2v& lo, half2v& hi) {
 template <int D, int kG>
 __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kernel(DecodeArgs a) {
   __shared__ Smem<D> sm;
-  const int chunk = blockIdx.x;
-  const int hg = blockIdx.y % a.head_groups;
-  const int sk = blockIdx.y / a.head_groups;  // sequence * Hkv + kv
-  const int seq = sk / a.hkv, kv = sk % a.hkv;
+  const int kv = blockIdx.x / a.head_groups, hg = blockIdx.x % a.head_groups;
+  const int chunk = blockIdx.y, seq = blockIdx.z;
   const int32_t* rec = a.plan + kHeaderLen + seq * kSeqStride;
   const int start = rec[kSeqStart], L = rec[kSeqLen];
   if (chunk * kChunk >= L) return;  // no keys here (the merge reads only live chunks)
@@ -185,12 +223,21 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
   // Every load of the workgroup is issued up front, branch-free (addresses of
   // keys past the sequence end are clamped to its last key: their scores are
   // masked and their P is 0), in the order of first use -- the scalars, the
-  // queries, this lane's key row, then this thread's share of the values --
+  // queries, the wave's key tile, then this thread's share of the values --
   // so the waits before the scores and before P.V each cover only what they
   // need, and the values stream in while the scores are computed.
-  const int t = chunk * 4 + w;              // this wave's key tile (sequence-local)
-  const int j = t * kBlockN + lane;         // this lane's key
-  const bool live = j < L;
+  //
+  // Key tile layout: kLanes = d / 16 lanes share a key row, each holding 16
+  // bytes (channels 16 sub ..) of rows kRows i + r, i < kLanes, so that one
+  // load instruction covers whole 128-byte lines (one row per lane asks the
+  // memory pipeline for 64 lines per instruction and streams a third slower).
+  // After the cross-lane reduction lane (r, sub) holds the score of key
+  // kRows sub + r of the tile.
+  constexpr int kLanes = D / 16, kRows = 64 / kLanes;
+  const int r = lane / kLanes, sub = lane % kLanes;
+  const int t = chunk * 4 + w;                        // this wave's key tile (sequence-local)
+  const int kk = w * kBlockN + sub * kRows + r;       // this lane's key within the chunk
+  const bool live = chunk * kChunk + kk < L;
   const bool tile_live = t * kBlockN < L;
   constexpr int kGroups = D / 4, kParts = kThreads / kGroups, kKeys = kChunk / kParts;
   const int c4 = tid % kGroups, part = tid / kGroups;
@@ -205,14 +252,11 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
 #pragma unroll
     for (int i = 0; i < D / 64; ++i)
       qv[u][i] = a.q[((size_t)seq * a.hq + h0 + min(w + 4 * u, G - 1)) * D + lane + 64 * i];
-  uint32_t kw[D / 4];
-  {
-    const int4v* krow = reinterpret_cast<const int4v*>(a.ki8 + ((size_t)(start + min(j, L - 1)) * a.hkv + kv) * D);
+  int4v kx[kLanes];
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      const int4v x = krow[i];
-      kw[4 * i] = x[0]; kw[4 * i + 1] = x[1]; kw[4 * i + 2] = x[2]; kw[4 * i + 3] = x[3];
-    }
+  for (int i = 0; i < kLanes; ++i) {
+    const int jr = min(t * kBlockN + kRows * i + r, L - 1);
+    kx[i] = *reinterpret_cast<const int4v*>(a.ki8 + ((size_t)(start + jr) * a.hkv + kv) * D + sub * 16);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the key loads ahead of the value loads
   // Values in the P.V layout: thread (4 channels c4, key part) holds its 4
@@ -253,33 +297,49 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
   }
   __syncthreads();
 
-  // Scores of this wave's key tile, one key per lane, in the log2 domain.
+  // Scores of this wave's key tile in the log2 domain: each lane's 16
+  // channels of its kLanes rows, then summed across the row's lanes.
   float xs[kG];
   if (bit) {
 #pragma unroll
     for (int h = 0; h < kG; ++h) {
       if (h >= G) break;
-      const uint32_t* qw = reinterpret_cast<const uint32_t*>(sm.qi[h]);
-      int acc = 0;
+      const int4v qq = *reinterpret_cast<const int4v*>(&sm.qi[h][sub * 16]);
+      int pr[kLanes];
 #pragma unroll
-      for (int i = 0; i < D / 4; ++i) acc = __builtin_amdgcn_sdot4((int)qw[i], (int)kw[i], acc, false);
-      // exact: |acc| <= 127^2 d < 2^24
+      for (int i = 0; i < kLanes; ++i) {
+        int acc = __builtin_amdgcn_sdot4(qq[0], kx[i][0], 0, false);
+        acc = __builtin_amdgcn_sdot4(qq[1], kx[i][1], acc, false);
+        acc = __builtin_amdgcn_sdot4(qq[2], kx[i][2], acc, false);
+        pr[i] = __builtin_amdgcn_sdot4(qq[3], kx[i][3], acc, false);
+      }
+      // exact: |sum| <= 127^2 d < 2^24
+      const int acc = transpose_reduce<kLanes>(pr, lane);
       const float f = (sm.sq[h] * s_k) * inv_sqrt_d;
       xs[h] = (float)acc * f * kLog2e;
     }
   } else {
-    half2v kh[D / 2];
+    half2v kh[kLanes][8];
 #pragma unroll
-    for (int i = 0; i < D / 4; ++i) i8x4_to_half(kw[i], kh[2 * i], kh[2 * i + 1]);
+    for (int i = 0; i < kLanes; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) i8x4_to_half((uint32_t)kx[i][e], kh[i][2 * e], kh[i][2 * e + 1]);
     const float f = s_k * inv_sqrt_d * kLog2e;
 #pragma unroll
     for (int h = 0; h < kG; ++h) {
       if (h >= G) break;
-      const half2v* qh = reinterpret_cast<const half2v*>(sm.qf[h]);
-      float acc = 0.f;
+      const half8 q0 = *reinterpret_cast<const half8*>(&sm.qf[h][sub * 16]);
+      const half8 q1 = *reinterpret_cast<const half8*>(&sm.qf[h][sub * 16 + 8]);
+      const half2v qh[8] = {q0.s01, q0.s23, q0.s45, q0.s67, q1.s01, q1.s23, q1.s45, q1.s67};
+      float pr[kLanes];
 #pragma unroll
-      for (int i = 0; i < D / 2; ++i) acc = __builtin_amdgcn_fdot2(qh[i], kh[i], acc, false);
-      xs[h] = acc * f;
+      for (int i = 0; i < kLanes; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_fdot2(qh[e], kh[i][e], acc, false);
+        pr[i] = acc;
+      }
+      xs[h] = transpose_reduce<kLanes>(pr, lane) * f;
     }
   }
 
@@ -299,7 +359,7 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
     const float m = fmaxf(fmaxf(sm.mx[0][h], sm.mx[1][h]), fmaxf(sm.mx[2][h], sm.mx[3][h]));
     // P rounded to fp16; the normaliser sums the same rounded values
     const float p = live ? (float)(_Float16)__builtin_amdgcn_exp2f(xs[h] - m) : 0.f;
-    sm.pv[h][w * kBlockN + lane] = (_Float16)p;
+    sm.pv[h][kk] = (_Float16)p;
     float l = p;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
@@ -518,11 +578,12 @@ int decode_launch(const int32_t* plan_h, const int32_t* plan_d, const void* q_f1
   const int grp = a.hq / a.hkv;
   a.head_groups = (grp + kMaxG - 1) / kMaxG;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const int64_t gy = (int64_t)batch * a.hkv * a.head_groups;
-  if (gy > 65535 || a.chunks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  if (batch > 65535) return fail(TILEMIX_EINVAL, "batch of %d sequences too large for one launch", batch);
+  if (a.chunks > 65535)
+    return fail(TILEMIX_EINVAL, "a sequence of more than %d keys is too long for one launch", 65535 * kChunk);
   const int d = plan_h[kHeadDim];
   if (a.chunks > 0) {
-    const dim3 grid(a.chunks, (unsigned)gy);
+    const dim3 grid((unsigned)(a.hkv * a.head_groups), (unsigned)a.chunks, (unsigned)batch);
     const int kg = std::min(grp, kMaxG);
     if (d == 64) launch_partial<64>(kg, grid, st, a);
     else launch_partial<128>(kg, grid, st, a);
