@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
   const int chunk = blockIdx.y, seq = blockIdx.z;
   const int32_t* rec = a.plan + kHeaderLen + seq * kSeqStride;
   const int start = rec[kSeqStart], L = rec[kSeqLen];
-  if (chunk * kChunk >= L) return;  // no keys here (the merge reads only live chunks)
+  if (chunk * kChunk >= L) return;  // no keys here (the merge folds in only live chunks)
   const int grp = a.hq / a.hkv;
   const int h0 = kv * grp + hg * kMaxG;
   const int G = kG < kMaxG ? kG : min(kMaxG, grp - hg * kMaxG);
@@ -416,52 +416,62 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
   }
 }
 
-// Merge of the chunks of one (sequence, query head), one wave each: the
-// online-softmax combination of partial states ([Routes, precision routing]:
-// one shared state), O = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i, written
-// as fp16.
+// Merge of the chunks of one (sequence, query head), one workgroup of
+// kMergeWaves(n) waves each: the online-softmax combination of partial
+// states ([Routes, precision routing]: one shared state),
+// O = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i, written as fp16.
+constexpr int kMergeBatch = 16;     // chunk records a wave requests together
+constexpr int kMergeMaxWaves = 8;
+
+// Waves per merge workgroup for a longest sequence of `chunks` chunks: one
+// batch of 16 chunk records per wave, up to 8 waves.
+inline int merge_waves(int64_t chunks) {
+  const int64_t b = (chunks + kMergeBatch - 1) / kMergeBatch;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kMergeMaxWaves, b));
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
-  const int wid = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (wid >= a.batch * a.hq) return;
-  const int seq = wid / a.hq, h = wid % a.hq;
-  const int L = a.plan[kHeaderLen + seq * kSeqStride + kSeqLen];
-  _Float16* o = a.out + ((size_t)seq * a.hq + h) * D;
-  if (L == 0) {
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) o[lane + 64 * i] = (_Float16)0.0f;
-    return;
-  }
-  const int n = (L + kChunk - 1) / kChunk;
+__global__ __launch_bounds__(64 * kMergeMaxWaves) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ float sm_m[kMergeMaxWaves], sm_l[kMergeMaxWaves];
+  __shared__ float sm_o[kMergeMaxWaves][D];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int seq = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
   const float* base = a.work + ((size_t)seq * a.hq + h) * a.chunks * (D + 2);
-  // One pass over batches of 16 chunks: a batch's (m, l) and O rows are
-  // requested together (none depends on the others) and the next batch is
-  // requested before this one is folded in, so the merge waits about one
-  // memory latency in all.  Earlier batches' (M, l, O) are rescaled as in the
-  // online softmax.
-  float M = -INFINITY, l = 0.f;
-  float acc[D / 64] = {};
+  // The sequence's length and the wave's first batch of records are
+  // requested together: the batch covers the chunks any sequence of the
+  // launch can have (all of them written or not), and the length decides
+  // afterwards which of them are live, so the merge waits one memory latency
+  // before folding.  Wave w takes batches w, w + nw, ...; a batch's (m, l)
+  // and O rows are requested together and the next batch before this one is
+  // folded in (online-softmax rescale across batches).
+  const int L = a.plan[kHeaderLen + seq * kSeqStride + kSeqLen];
   float2 ml, mln;
-  float ov[16][D / 64], ovn[16][D / 64];
-  auto fetch = [&](int i0, float2& m2, float (&dst)[16][D / 64]) {
-    const int nb = min(16, n - i0);
+  float ov[kMergeBatch][D / 64], ovn[kMergeBatch][D / 64];
+  auto fetch = [&](int i0, float2& m2, float (&dst)[kMergeBatch][D / 64]) {
+    const int nb = min(kMergeBatch, a.chunks - i0);  // records inside the workspace
     m2 = lane < nb ? *reinterpret_cast<const float2*>(base + (size_t)(i0 + lane) * (D + 2))
                    : make_float2(-INFINITY, 0.f);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < kMergeBatch; ++i)
 #pragma unroll
       for (int c = 0; c < D / 64; ++c)
         dst[i][c] = i < nb ? base[(size_t)(i0 + i) * (D + 2) + 2 + lane + 64 * c] : 0.f;
   };
-  fetch(0, mln, ovn);
-  for (int i0 = 0; i0 < n; i0 += 16) {
+  const int step = nw * kMergeBatch;
+  int i0 = w * kMergeBatch;
+  if (i0 < a.chunks) fetch(i0, mln, ovn);
+  const int n = (L + kChunk - 1) / kChunk;  // live chunks of this sequence
+  float M = -INFINITY, l = 0.f;
+  float acc[D / 64] = {};
+  for (; i0 < n; i0 += step) {
     ml = mln;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < kMergeBatch; ++i)
 #pragma unroll
       for (int c = 0; c < D / 64; ++c) ov[i][c] = ovn[i][c];
-    if (i0 + 16 < n) fetch(i0 + 16, mln, ovn);
-    const int nb = min(16, n - i0);
+    if (i0 + step < n) fetch(i0 + step, mln, ovn);
+    const int nb = min(kMergeBatch, n - i0);
+    if (lane >= nb) ml = make_float2(-INFINITY, 0.f);  // records past the sequence's end
     float mb = ml.x;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
@@ -475,14 +485,35 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) acc[c] *= alpha;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kMergeBatch; ++i) {
       const float wi = __shfl(wl, i);
+      if (i < nb) {
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) acc[c] += wi * ov[i][c];
+        for (int c = 0; c < D / 64; ++c) acc[c] += wi * ov[i][c];
+      }
     }
     M = Mn;
   }
-  const float inv = 1.0f / l;
+  if (nw > 1) {  // combine the waves' states
+    if (lane == 0) { sm_m[w] = M; sm_l[w] = l; }
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) sm_o[w][lane + 64 * c] = acc[c];
+    __syncthreads();
+    if (w != 0) return;
+    float Mt = -INFINITY;
+    for (int u = 0; u < nw; ++u) Mt = fmaxf(Mt, sm_m[u]);
+    l = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) acc[c] = 0.f;
+    for (int u = 0; u < nw; ++u) {
+      const float wu = sm_m[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm_m[u] - Mt);
+      l += wu * sm_l[u];
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) acc[c] += wu * sm_o[u][lane + 64 * c];
+    }
+  }
+  _Float16* o = a.out + ((size_t)seq * a.hq + h) * D;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;  // an empty sequence gives zeros
 #pragma unroll
   for (int c = 0; c < D / 64; ++c) o[lane + 64 * c] = (_Float16)(acc[c] * inv);
 }
@@ -590,11 +621,12 @@ int decode_launch(const int32_t* plan_h, const int32_t* plan_d, const void* q_f1
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
-  const unsigned merge = (unsigned)(((int64_t)batch * a.hq + 3) / 4);  // one wave per (sequence, head)
+  const unsigned merge = (unsigned)((int64_t)batch * a.hq);  // one workgroup per (sequence, head)
+  const dim3 mblock(64 * merge_waves(a.chunks));
   if (d == 64)
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(merge), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(merge), mblock, 0, st, a);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(merge), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(merge), mblock, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode merge launch");
   return TILEMIX_OK;
