@@ -666,6 +666,106 @@ def cpu_baseline(q, k, v, cu, spec, template, coverage, budget_s=20.0, full_head
             "full_oracle": full}
 
 
+def hw_probes(reps=7):
+    """Hardware-rate probes (libtilemix_probes.so, timing-only kernels) behind
+    the kernels' cost model: shader clock, vector-ALU issue per wave count,
+    the matrix pipe beside the vector ALU, direct HBM/L2->LDS copies, LDS
+    reads, and the decode step's HBM read patterns.  Median of `reps` timed
+    launches (events on the current stream) after two untimed ones."""
+    import ctypes
+    import statistics
+
+    import torch
+
+    from mixed_precision_attention_amd import build as _b
+
+    if not os.path.exists(_b.PROBES_PATH):
+        raise SystemExit("libtilemix_probes.so is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(_b.PROBES_PATH)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.tilemix_probe_valu.argtypes = [ci, ci, ci, vp, vp]
+    lib.tilemix_probe_coexec.argtypes = [ci, ci, ci, vp, vp]
+    lib.tilemix_probe_copy.argtypes = [vp, ci, ci, ci, ci, vp, vp]
+    lib.tilemix_probe_lds.argtypes = [ci, ci, ci, vp, vp]
+    lib.tilemix_probe_clock.argtypes = [ci, ci, vp, vp]
+    lib.tilemix_probe_read.argtypes = [ci, vp, vp, vp, vp]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cus = 256
+
+    def timed(launch):
+        ts = []
+        for r in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = launch()
+            e1.record()
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+            torch.cuda.synchronize()
+            if r >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        return statistics.median(ts)
+
+    out = torch.zeros(2048 * 512, dtype=torch.int32, device="cuda")
+    res = {}
+    # shader clock under an all-CU FMA load
+    stamps = torch.zeros(4, dtype=torch.int64, device="cuda")
+    if lib.tilemix_probe_clock(cus * 4, 200000, stamps.data_ptr(), stream) != 0:
+        raise RuntimeError("clock probe launch failed")
+    torch.cuda.synchronize()
+    t0, t1, r0, r1 = stamps.tolist()
+    clk = (t1 - t0) / max(r1 - r0, 1) * 1e8
+    res["shader_clock_ghz"] = round(clk / 1e9, 3)
+    # vector-ALU issue: SIMD cycles per instruction, and each wave's issue interval
+    iters = 4000
+    valu = {}
+    for op, name in ((0, "fma"), (1, "exp")):
+        for w in (1, 2, 3, 4, 8):
+            us = timed(lambda: lib.tilemix_probe_valu(op, cus * w, iters, out.data_ptr(), stream))
+            per = us * 1e-6 * clk / (w * iters * 16)
+            valu[f"{name}_{w}w"] = {"us": round(us, 1), "simd_cycles_per_instr": round(per, 2),
+                                    "wave_issue_interval": round(per * w, 2)}
+    res["valu_16_chains"] = valu
+    # matrix pipe beside the vector ALU (one wave of each kind per SIMD)
+    iters = 4000
+    co = {name: round(timed(lambda: lib.tilemix_probe_coexec(mode, cus, iters, out.data_ptr(), stream)), 1)
+          for mode, name in ((1, "mfma_only_us"), (2, "fma_only_us"), (0, "both_us"))}
+    co["serial_us"] = round(co["mfma_only_us"] + co["fma_only_us"], 1)
+    res["mfma_beside_valu"] = co
+    # direct copies into LDS: bytes per clock per CU with 1..16 1-KB copies in flight per wave
+    cp = {}
+    for src_mb in (2, 256):
+        src = torch.randint(-127, 127, (src_mb << 20,), dtype=torch.int8, device="cuda")
+        for batch in (1, 2, 4, 8, 16):
+            it = 512 // batch
+            us = timed(lambda: lib.tilemix_probe_copy(src.data_ptr(), src_mb * 1024, cus, it, batch,
+                                                      out.data_ptr(), stream))
+            total = cus * 8 * it * batch * 1024
+            cp[f"src{src_mb}MB_batch{batch}"] = round(total / cus / (us * 1e-6 * clk), 1)
+        del src
+    res["copy_to_lds_bytes_per_clk_per_cu"] = cp
+    # LDS reads (8 waves per CU, conflict-free)
+    iters = 200
+    ld = {}
+    for op, name in ((0, "ds_read_b128"), (1, "ds_read_b64_tr_b16")):
+        us = timed(lambda: lib.tilemix_probe_lds(op, cus, iters, out.data_ptr(), stream))
+        ld[name] = round(8 * 16384 * iters / (us * 1e-6 * clk), 1)
+    res["lds_read_bytes_per_clk_per_cu"] = ld
+    # the decode step's HBM read patterns over a 2 x 32 MiB int8 cache
+    n = 32768 * 8 * 128
+    kbuf = torch.randint(-127, 127, (n,), dtype=torch.int8, device="cuda")
+    vbuf = torch.randint(-127, 127, (n,), dtype=torch.int8, device="cuda")
+    rd = {}
+    for pat, name in ((0, "contiguous"), (1, "key_row_per_lane"), (2, "8_lanes_per_key_row"),
+                      (3, "8_lanes_per_key_row_head_fastest")):
+        us = timed(lambda: lib.tilemix_probe_read(pat, kbuf.data_ptr(), vbuf.data_ptr(), out.data_ptr(), stream))
+        rd[name] = {"us": round(us, 2), "tb_per_s": round(2 * n / us / 1e6, 2)}
+    res["decode_read_patterns_64MiB"] = rd
+    res["note"] = ("cycles at the measured shader clock; launches timed with events, so each time "
+                   "includes a few microseconds of launch latency")
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -703,6 +803,9 @@ def main(argv=None):
                          "profiles/prefill_<workload>_traffic.json and exit")
     ap.add_argument("--copy-size", type=int, default=512 << 20,
                     help="bytes the --copy-bytes run copied (for --write-traffic)")
+    ap.add_argument("--hw-probes", action="store_true",
+                    help="run only the hardware-rate probes (libtilemix_probes.so) and print their "
+                         "results as one JSON line")
     ap.add_argument("--profile-command", default="",
                     help="command line recorded in the --write-traffic summary")
     args = ap.parse_args(argv)
@@ -725,6 +828,10 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+
+    if args.hw_probes:
+        print(json.dumps({"hw_probes": hw_probes()}), flush=True)
+        return 0
 
     if args.copy_bytes:
         n = args.copy_bytes // 16 * 16

@@ -37,6 +37,12 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["tilemix_host.cpp", "tilemix_kernels.hip", "tilemix_decode.hip", "tilemix_adaptive.hip",
            "tilemix_stack.hip"]
 
+# The hardware-rate probes (timing-only kernels for the measurement record),
+# a library of their own.
+PROBES_NAME = "libtilemix_probes.so"
+PROBES_PATH = os.path.join(HERE, PROBES_NAME)
+PROBES_SOURCES = ["tilemix_probes.hip"]
+
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -62,13 +68,14 @@ SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize
 DEBUG_FLAGS = ["-DTILEMIX_DEBUG_PLAN"]
 
 
-def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH, link_flags=None) -> str:
+def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH, link_flags=None,
+          sources=None) -> str:
     """Compile every source into ``libtilemix.so`` (at ``out_path``); returns its path."""
     out_dir = os.path.dirname(out_path)
     os.makedirs(out_dir, exist_ok=True)
     out_tmp = out_path + ".tmp"
     objs = []
-    for src in SOURCES:
+    for src in sources or SOURCES:
         obj = os.path.join(out_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "c++"]
         cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC,
@@ -81,6 +88,11 @@ def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH, lin
     for obj in objs:
         os.remove(obj)
     return out_path
+
+
+def build_probes(verbose: bool = False) -> str:
+    """The hardware-rate probe library ``libtilemix_probes.so``, next to this file."""
+    return build(verbose, out_path=PROBES_PATH, sources=PROBES_SOURCES)
 
 
 def build_checking(kind: str, verbose: bool = False) -> str:
@@ -112,3 +124,4 @@ if __name__ == "__main__":
         print(build_checking("host_sanitize", verbose=True))
     else:
         print(build(verbose=True))
+        print(build_probes(verbose=True))

@@ -29,6 +29,22 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+PROBES_LIB = os.path.join(os.path.dirname(tm.LIB_PATH), "libtilemix_probes.so")
+
+
+@pytest.mark.skipif(not os.path.exists(PROBES_LIB), reason="libtilemix_probes.so not built")
+def test_probe_library_exports_every_declared_symbol():
+    text = open(os.path.join(ROOT, "include", "tilemix_probes.h")).read()
+    names = sorted(set(re.findall(r"\b(tilemix_probe_[a-z0-9_]+)\s*\(", text)))
+    assert len(names) == 6
+    lib = ctypes.CDLL(PROBES_LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    # the attention library exports none of them
+    main = ctypes.CDLL(tm.LIB_PATH)
+    assert not any(hasattr(main, n) for n in names)
+
+
 @pytest.mark.parametrize("template", oracle.TEMPLATES)
 def test_routing_bit_exact_with_oracle(template):
     for lens in ([256], [1], [130], [1000], [4096], [8192], [300, 0, 77, 129, 2049],
