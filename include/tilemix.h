@@ -308,7 +308,8 @@ int tilemix_decode_workspace_size(const int32_t* plan_h, int64_t* bytes);
  * scratch of at least tilemix_decode_workspace_size bytes (its contents are
  * overwritten); out_f16: device [B, Hq, d] (zeros for an empty sequence).
  * Errors: EINVAL for a missing or misaligned pointer, a small workspace, more
- * than 65,535 sequences or a sequence of more than 65,535 * 256 keys. */
+ * than 65,535 sequences, a sequence of more than 65,535 * 256 keys, or
+ * Hkv * d * 256 above 2^31 - 1 bytes. */
 int tilemix_decode_varlen(const int32_t* plan_h, const int32_t* plan_d, const void* q_f16,
                           const int8_t* k_i8, const int8_t* v_i8, const float* k_scale,
                           const float* v_scale, const uint64_t* words_d, void* workspace,

@@ -150,7 +150,7 @@ struct Smem {
   _Float16 qf[kMaxG][D];                            // fp16 queries
   int8_t qi[kMaxG][D];                              // int8 queries
   float sq[kMaxG];                                  // query scales
-  float mx[4][kMaxG];                               // per-wave maxima
+  float mx[4][kMaxG];                               // per-wave (key tile) maxima
   float ls[4][kMaxG];                               // per-wave sums of P
   _Float16 pv[kMaxG][kChunk];                       // fp16-rounded P
   float part[4][kMaxG][D];                          // per-wave P.V sums
@@ -252,21 +252,29 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
 #pragma unroll
     for (int i = 0; i < D / 64; ++i)
       qv[u][i] = a.q[((size_t)seq * a.hq + h0 + min(w + 4 * u, G - 1)) * D + lane + 64 * i];
+  // The chunk's rows of this head through buffer resources sized to the rows
+  // before the sequence end: a row at or past it lies outside and reads as
+  // zero (its score is masked and its P is 0), and each load's address is
+  // one lane offset (the range check covers the lane offset, so the row
+  // step goes there, not in the scalar offset).
+  const uint32_t stride = (uint32_t)(a.hkv * D);      // bytes between consecutive rows
+  const int nrows = min(kChunk, L - chunk * kChunk);  // >= 1
+  const size_t row0 = ((size_t)(start + chunk * kChunk) * a.hkv + kv) * D;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.ki8 + row0), (short)0, (int)(nrows * stride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.vi8 + row0), (short)0, (int)(nrows * stride), 0x00020000);
   int4v kx[kLanes];
+  const uint32_t koff = (uint32_t)(w * kBlockN + r) * stride + sub * 16;
 #pragma unroll
-  for (int i = 0; i < kLanes; ++i) {
-    const int jr = min(t * kBlockN + kRows * i + r, L - 1);
-    kx[i] = *reinterpret_cast<const int4v*>(a.ki8 + ((size_t)(start + jr) * a.hkv + kv) * D + sub * 16);
-  }
+  for (int i = 0; i < kLanes; ++i) kx[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + kRows * i * stride, 0, 0);
   __builtin_amdgcn_sched_barrier(0);  // keep the key loads ahead of the value loads
   // Values in the P.V layout: thread (4 channels c4, key part) holds its 4
   // channels of each of its keys (a wave reads whole 128-byte rows).
   uint32_t vreg[kKeys];
+  const uint32_t voff = (uint32_t)(part * kKeys) * stride + c4 * 4;
 #pragma unroll
-  for (int k = 0; k < kKeys; ++k) {
-    const int jj = min(chunk * kChunk + part * kKeys + k, L - 1);
-    vreg[k] = *reinterpret_cast<const uint32_t*>(a.vi8 + ((size_t)(start + jj) * a.hkv + kv) * D + c4 * 4);
-  }
+  for (int k = 0; k < kKeys; ++k) vreg[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(vrs, voff + k * stride, 0, 0);
   const float s_vp = vt * kBlockN < L ? s_vp_raw : 0.f;
   const float s_k = tile_live ? s_k_raw : 0.f;
   const bool bit = tile_live && ((word >> (t / rec[kSeqG])) & 1ull);
@@ -343,34 +351,37 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
     }
   }
 
-  // Chunk softmax state per head (log2 domain, relative to the chunk max).
+  // Softmax state per wave and head over the wave's own key tile (log2
+  // domain, relative to the tile's maximum): P is rounded to fp16 against it
+  // and the normaliser sums the same rounded values.  The wave reads back
+  // only the P it wrote, so no workgroup barrier stands between a wave's
+  // keys and its P.V; the four tiles' states are combined at the end,
+  // rescaled to the chunk maximum (the online-softmax step with the key tile
+  // as the unit).
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
     if (h >= G) break;
     float m = live ? xs[h] : -INFINITY;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) sm.mx[w][h] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < kG; ++h) {
-    if (h >= G) break;
-    const float m = fmaxf(fmaxf(sm.mx[0][h], sm.mx[1][h]), fmaxf(sm.mx[2][h], sm.mx[3][h]));
-    // P rounded to fp16; the normaliser sums the same rounded values
     const float p = live ? (float)(_Float16)__builtin_amdgcn_exp2f(xs[h] - m) : 0.f;
     sm.pv[h][kk] = (_Float16)p;
     float l = p;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-    if (lane == 0) sm.ls[w][h] = l;
+    if (lane == 0) {  // read only after the final barrier
+      sm.mx[w][h] = m;
+      sm.ls[w][h] = l;
+    }
   }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // P.V with the dequantised values: each thread sums its keys two at a time
-  // with fp16 pair dot products (fp16 P and int8 values are exact in fp16;
-  // products exact, fp32 sums), then applies its key tile's value scale (a
-  // part lies inside one key tile).
+  // P.V with the dequantised values over the wave's own 64 keys: each thread
+  // sums its keys two at a time with fp16 pair dot products (fp16 P and int8
+  // values are exact in fp16; products exact, fp32 sums), then applies its
+  // key tile's value scale (a part lies inside one key tile).
   float acc[kG][4] = {};
 #pragma unroll
   for (int k = 0; k < kKeys; k += 2) {
@@ -388,7 +399,7 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
     }
   }
   // Sum the parts: lanes l, l + kGroups, ... of a wave hold the same
-  // channels, then the four waves through LDS.
+  // channels; then the four waves' states through LDS.
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
     if (h >= G) break;
@@ -401,17 +412,24 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
     }
   }
   __syncthreads();
-  // Workspace record of (sequence, head, chunk): m, l, O[D] (unnormalised).
+  // Workspace record of (sequence, head, chunk): m, l, O[D] (unnormalised),
+  // O = sum over the tiles of 2^(m_w - m) O_w.
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D, c = idx % D;
-    float o = 0.f;
+    const float m = fmaxf(fmaxf(sm.mx[0][h], sm.mx[1][h]), fmaxf(sm.mx[2][h], sm.mx[3][h]));
+    float o = 0.f, l = 0.f;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) o += sm.part[p][h][c];
+    for (int p = 0; p < 4; ++p) {
+      const float mp = sm.mx[p][h];
+      const float sc = mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp - m);
+      o += sc * sm.part[p][h][c];
+      l += sc * sm.ls[p][h];
+    }
     float* rec_out = a.work + (((size_t)seq * a.hq + h0 + h) * a.chunks + chunk) * (D + 2);
     rec_out[2 + c] = o;
     if (c == 0) {
-      rec_out[0] = fmaxf(fmaxf(sm.mx[0][h], sm.mx[1][h]), fmaxf(sm.mx[2][h], sm.mx[3][h]));
-      rec_out[1] = (sm.ls[0][h] + sm.ls[1][h]) + (sm.ls[2][h] + sm.ls[3][h]);
+      rec_out[0] = m;
+      rec_out[1] = l;
     }
   }
 }
@@ -610,6 +628,8 @@ int decode_launch(const int32_t* plan_h, const int32_t* plan_d, const void* q_f1
   a.head_groups = (grp + kMaxG - 1) / kMaxG;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (batch > 65535) return fail(TILEMIX_EINVAL, "batch of %d sequences too large for one launch", batch);
+  if ((int64_t)a.hkv * plan_h[kHeadDim] * kChunk > 0x7fffffff)
+    return fail(TILEMIX_EINVAL, "%d KV heads: a 256-row chunk of the cache exceeds 2 GiB", a.hkv);
   if (a.chunks > 65535)
     return fail(TILEMIX_EINVAL, "a sequence of more than %d keys is too long for one launch", 65535 * kChunk);
   const int d = plan_h[kHeadDim];
