@@ -481,6 +481,36 @@ def bench_sweep(workload, templates, coverages, steps=20):
     return {"workload": workload, "steps": steps, "templates": res}
 
 
+def bench_lengths(shapes=((32, 1024), (16, 2048), (8, 4096), (4, 8192), (2, 16384)), template="sptrans",
+                  coverage=7500, steps=20):
+    """Prefill at a fixed 32,768 tokens split into B sequences of L (3B head
+    shape: Hq 24, Hkv 8, d 128, outlier channels, SpTrans 75%, Q quantised in
+    the kernel): time per attention call in the path's order and the
+    coverage-weighted MFMA roofline fraction, to show how the per-unit
+    prologue and epilogue weigh at short sequences."""
+    import torch
+    import mixed_precision_attention_amd as tm
+    import synth
+    hq, hkv, d = 24, 8, 128
+    rows = []
+    for B, L in shapes:
+        q, k, v, cu = synth.make_qkv([L] * B, hq, hkv, d, outliers=True, seed=0)
+        qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+        del q, k, v
+        tp = tm.TileMixPrefill(cu, hq, hkv, d, template, coverage)
+        out = torch.empty_like(qd)
+        ms = min(time_in_pipeline(lambda: tp.quantize_k(kd), lambda: tp.attend_qinline(qd, kd, vd, out), steps)
+                 for _ in range(2))
+        P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
+        t_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
+        rows.append({"batch": B, "seq_len": L, "prefill_ms": round(ms, 4),
+                     "tokens_per_s": B * L / (ms * 1e-3), "frac": round(t_roof / (ms * 1e-3), 4)})
+        del qd, kd, vd, out, tp
+        torch.cuda.empty_cache()
+    return {"tokens": 32768, "hq": hq, "hkv": hkv, "head_dim": d, "template": template,
+            "coverage_bp": coverage, "steps": steps, "runs": rows}
+
+
 def decode_bytes(cu, hq, hkv, d, tq, tk):
     """Algorithmic HBM bytes of one decode step: the INT8 cache (K and V) and
     its scales read once, the routing words, the queries read and the output
@@ -803,6 +833,9 @@ def main(argv=None):
                          "profiles/prefill_<workload>_traffic.json and exit")
     ap.add_argument("--copy-size", type=int, default=512 << 20,
                     help="bytes the --copy-bytes run copied (for --write-traffic)")
+    ap.add_argument("--length-sweep", action="store_true",
+                    help="run only the sequence-length sweep (32,768 tokens as 32x1k ... 2x16k) and print it "
+                         "as one JSON line")
     ap.add_argument("--hw-probes", action="store_true",
                     help="run only the hardware-rate probes (libtilemix_probes.so) and print their "
                          "results as one JSON line")
@@ -831,6 +864,10 @@ def main(argv=None):
 
     if args.hw_probes:
         print(json.dumps({"hw_probes": hw_probes()}), flush=True)
+        return 0
+
+    if args.length_sweep:
+        print(json.dumps({"length_sweep": bench_lengths()}), flush=True)
         return 0
 
     if args.copy_bytes:
