@@ -718,6 +718,7 @@ def hw_probes(reps=7):
     lib.tilemix_probe_copy.argtypes = [vp, ci, ci, ci, ci, vp, vp]
     lib.tilemix_probe_lds.argtypes = [ci, ci, ci, vp, vp]
     lib.tilemix_probe_clock.argtypes = [ci, ci, vp, vp]
+    lib.tilemix_probe_skeleton.argtypes = [ci, ci, ci, vp, vp]
     lib.tilemix_probe_read.argtypes = [ci, vp, vp, vp, vp]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     cus = 256
@@ -762,6 +763,15 @@ def hw_probes(reps=7):
           for mode, name in ((1, "mfma_only_us"), (2, "fma_only_us"), (0, "both_us"))}
     co["serial_us"] = round(co["mfma_only_us"] + co["fma_only_us"], 1)
     res["mfma_beside_valu"] = co
+    # the prefill wave-tile's matrix skeleton (QK int8 -> convert -> pack -> PV f16), no loads:
+    # matrix-pipe utilisation at the published peaks (768 cycles per iteration)
+    iters = 2000
+    sk = {}
+    for w in (1, 2):
+        for extra in (0, 64, 128):
+            us = timed(lambda: lib.tilemix_probe_skeleton(extra, cus * w, iters, out.data_ptr(), stream))
+            sk[f"{w}w_extra{extra}"] = round(768 * iters * w / (us * 1e-6 * clk), 3)
+    res["skeleton_mfma_utilisation"] = sk
     # direct copies into LDS: bytes per clock per CU with 1..16 1-KB copies in flight per wave
     cp = {}
     for src_mb in (2, 256):

@@ -43,6 +43,13 @@ int tilemix_probe_copy(const void* src, int src_kb, int blocks, int iters, int b
  * per iteration with op 0 ds_read_b128 or op 1 ds_read_b64_tr_b16. */
 int tilemix_probe_lds(int op, int blocks, int iters, int* out, void* stream);
 
+/* Matrix skeleton of one prefill wave-tile per iteration, operands in
+ * registers: 8 chained 32x32x32 int8 MFMAs, the scores converted to fp32,
+ * `extra` (0, 64 or 128) further FMAs, packed to fp16, 16 32x32x16 f16
+ * MFMAs (768 matrix cycles at the published peaks); `blocks` groups of 256
+ * threads. */
+int tilemix_probe_skeleton(int extra, int blocks, int iters, float* out, void* stream);
+
 /* Shader clock: `blocks` groups of 256 threads run FMA chains for `iters`
  * steps; group 0 writes the shader-clock counter (s_memtime) before and
  * after into out[0], out[1] and the 100 MHz real-time counter into out[2],

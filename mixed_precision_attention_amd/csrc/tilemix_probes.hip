@@ -18,6 +18,8 @@ namespace tilemix_probe {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int16v __attribute__((ext_vector_type(16)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short2v __attribute__((ext_vector_type(2)));
 
@@ -222,6 +224,63 @@ __global__ __launch_bounds__(256) void read_kernel(const int8_t* K, const int8_t
 }
 
 // --------------------------------------------------------------------------
+// Matrix skeleton of one prefill wave-tile, operands in registers (no loads):
+// Q.K^T as 8 chained 32x32x32 int8 MFMAs (two 32-key blocks), the 32 int32
+// scores per lane converted to fp32, EXTRA further FMAs spread over them,
+// packed to fp16, then P.V as 16 32x32x16 f16 MFMAs into four accumulators.
+// 768 matrix cycles per iteration at the published peak rates.
+// --------------------------------------------------------------------------
+template <int EXTRA>
+__global__ __launch_bounds__(256) void skeleton_kernel(float* out, int iters, float c) {
+  const int lane = threadIdx.x & 63;
+  int4v kf[4], qb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kf[i] = (int4v){lane + i, 3 * lane + i, 5 * lane - i, 7 * lane} & 0x3f3f3f3f;
+    qb[i] = (int4v){lane ^ i, lane * 11, i * 13, lane + 17} & 0x3f3f3f3f;
+  }
+  half8 vf[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vf[db][j] = (_Float16)(0.001f * (lane + j + db));
+  float16v o[4] = {};
+  for (int it = 0; it < iters; ++it) {
+    int16v acc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      acc[kb] = (int16v){};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[(kk + kb) & 3], qb[kk], acc[kb], 0, 0, 0);
+    }
+    float f[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      f[i] = (float)acc[0][i] * c;
+      f[16 + i] = (float)acc[1][i] * c;
+    }
+#pragma unroll
+    for (int e = 0; e < EXTRA; ++e) f[e & 31] = __builtin_fmaf(f[e & 31], c, 1e-3f);
+    half8 pf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[ks][j] = (_Float16)f[ks * 8 + j];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pf[ks], o[db], 0, 0, 0);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += o[db][i];
+  if (__builtin_bit_cast(int, r) == kMagic) out[blockIdx.x * 256 + threadIdx.x] = r;
+}
+
+// --------------------------------------------------------------------------
 // Shader clock: every group runs FMA chains for `iters` steps; group 0's
 // first wave stamps the shader-clock counter (s_memtime) and the 100 MHz
 // real-time counter (s_memrealtime) before and after, out[0..3].
@@ -289,6 +348,18 @@ int tilemix_probe_lds(int op, int blocks, int iters, int* out, void* stream) {
   if (op == 0) hipLaunchKernelGGL(lds_kernel<0>, dim3(blocks), dim3(512), 131072, st, out, iters);
   else if (op == 1) hipLaunchKernelGGL(lds_kernel<1>, dim3(blocks), dim3(512), 131072, st, out, iters);
   else return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+int tilemix_probe_skeleton(int extra, int blocks, int iters, float* out, void* stream) {
+  if (blocks <= 0 || iters <= 0 || out == nullptr) return -1;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (extra) {
+    case 0: hipLaunchKernelGGL(skeleton_kernel<0>, dim3(blocks), dim3(256), 0, st, out, iters, 1e-6f); break;
+    case 64: hipLaunchKernelGGL(skeleton_kernel<64>, dim3(blocks), dim3(256), 0, st, out, iters, 1e-6f); break;
+    case 128: hipLaunchKernelGGL(skeleton_kernel<128>, dim3(blocks), dim3(256), 0, st, out, iters, 1e-6f); break;
+    default: return -1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

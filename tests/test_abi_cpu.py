@@ -36,7 +36,7 @@ PROBES_LIB = os.path.join(os.path.dirname(tm.LIB_PATH), "libtilemix_probes.so")
 def test_probe_library_exports_every_declared_symbol():
     text = open(os.path.join(ROOT, "include", "tilemix_probes.h")).read()
     names = sorted(set(re.findall(r"\b(tilemix_probe_[a-z0-9_]+)\s*\(", text)))
-    assert len(names) == 6
+    assert len(names) == 7
     lib = ctypes.CDLL(PROBES_LIB)
     for n in names:
         assert hasattr(lib, n), n
