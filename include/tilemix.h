@@ -208,7 +208,9 @@ int tilemix_prefill_varlen(const int32_t* plan_h, const int32_t* plan_d, const v
 /* Key half of tilemix_quantize_qk (device): the same K blocks, scales and
  * codes, for use with tilemix_prefill_varlen_qinline.
  * Inputs:  k_f16 [T, Hkv, d] (device).
- * Outputs: k_i8 [T, Hkv, d] (device int8), k_scale float[Hkv][total_k_tiles]. */
+ * Outputs: k_i8 [T, Hkv, d] (device int8), k_scale float[Hkv][total_k_tiles].
+ * Errors: EINVAL for a missing or misaligned pointer, more than 65,535
+ * sequences, or Hkv * d * 2 * 64 above 2^31 - 1 bytes. */
 int tilemix_quantize_k(const int32_t* plan_h, const int32_t* plan_d, const void* k_f16, int8_t* k_i8,
                        float* k_scale, void* hip_stream);
 

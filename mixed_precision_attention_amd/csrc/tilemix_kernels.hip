@@ -83,25 +83,20 @@ __device__ inline int quant_code_i8(float x, float rs, float s) {
   return (int)__builtin_amdgcn_fmed3f(qf, -127.f, 127.f);
 }
 
+// The block's absmax over the values this thread holds (thread tid holds
+// the 16-byte chunks tid + i * kThreads of the block, rows past the block's
+// end as zeros), its scale, and the codes of the rows before the end.
 template <int D, int BLK>
-__device__ inline void quantize_block(const _Float16* src, int8_t* dst, float* scale_out,
+__device__ inline void quantize_store(const half8 (&vals)[BLK * (D / 8) / kThreads], int8_t* dst, float* scale_out,
                                       int row_stride, int nrows, float* red) {
   constexpr int kChunksPerRow = D / 8;                 // 16-byte chunks
-  constexpr int kChunks = BLK * kChunksPerRow;
-  constexpr int kPerThread = kChunks / kThreads;
+  constexpr int kPerThread = BLK * kChunksPerRow / kThreads;
   const int tid = threadIdx.x;
-  half8 vals[kPerThread];
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int idx = tid + i * kThreads;
-    const int r = idx / kChunksPerRow, cc = idx % kChunksPerRow;
-    half8 v = {};
-    if (r < nrows) v = *reinterpret_cast<const half8*>(src + (size_t)r * row_stride + cc * 8);
-    vals[i] = v;
+  for (int i = 0; i < kPerThread; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)v[j]));
-  }
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)vals[i][j]));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((tid & 63) == 0) red[tid >> 6] = amax;
@@ -123,6 +118,58 @@ __device__ inline void quantize_block(const _Float16* src, int8_t* dst, float* s
     }
     *reinterpret_cast<uint2*>(dst + (size_t)r * row_stride + cc * 8) = make_uint2(lo, hi);
   }
+}
+
+template <int D, int BLK>
+__device__ inline void quantize_block(const _Float16* src, int8_t* dst, float* scale_out,
+                                      int row_stride, int nrows, float* red) {
+  constexpr int kChunksPerRow = D / 8;                 // 16-byte chunks
+  constexpr int kPerThread = BLK * kChunksPerRow / kThreads;
+  const int tid = threadIdx.x;
+  half8 vals[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / kChunksPerRow, cc = idx % kChunksPerRow;
+    half8 v = {};
+    if (r < nrows) v = *reinterpret_cast<const half8*>(src + (size_t)r * row_stride + cc * 8);
+    vals[i] = v;
+  }
+  quantize_store<D, BLK>(vals, dst, scale_out, row_stride, nrows, red);
+}
+
+// Key blocks alone, one workgroup per (key tile of a sequence, KV head) with
+// the sequence taken from the grid (no search over the sequence table) and
+// the KV head fastest in the launch order (neighbouring workgroups read
+// neighbouring bytes of the same rows).  The block's rows come through a
+// buffer resource sized to the rows before the sequence end, so every load
+// is issued at once without a branch (rows past the end read as zero, as
+// quantize_block's guarded loads give them).  Codes and scales are those of
+// quantize_block, bit for bit.
+template <int D>
+__global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
+  __shared__ float red[4];
+  constexpr int kChunksPerRow = D / 8;
+  constexpr int kPerThread = kBlockN * kChunksPerRow / kThreads;
+  const int head = blockIdx.x % a.hkv, local = blockIdx.x / a.hkv, seq = blockIdx.y;
+  const int32_t* rec = a.plan + kHeaderLen + seq * kSeqStride;
+  const int L = rec[kSeqLen];
+  if (local * kBlockN >= L) return;
+  const int nrows = min(kBlockN, L - local * kBlockN);
+  const int stride = a.hkv * D;  // elements between consecutive rows
+  const size_t base = ((size_t)(rec[kSeqStart] + local * kBlockN) * a.hkv + head) * D;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k + base), (short)0, (int)((size_t)nrows * stride * sizeof(_Float16)), 0x00020000);
+  half8 vals[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    const int r = idx / kChunksPerRow, cc = idx % kChunksPerRow;
+    vals[i] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, (uint32_t)((r * stride + cc * 8) * sizeof(_Float16)), 0, 0));
+  }
+  quantize_store<D, kBlockN>(vals, a.ki8 + base, a.ks + (size_t)head * a.tk + rec[kSeqKtOff] + local, stride,
+                             nrows, red);
 }
 
 template <int D>
@@ -1282,13 +1329,23 @@ int tilemix_quantize_k(const int32_t* plan_h, const int32_t* plan_d, const void*
   a.batch = plan_h[kBatch];
   a.tq = plan_h[kTotalQTiles];
   a.tk = plan_h[kTotalKTiles];
-  const int64_t blocks = (int64_t)a.tk * a.hkv;
-  if (blocks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  // grid: (key tiles of the longest sequence x KV heads, sequences)
+  int64_t max_tn = 0;
+  for (int32_t s = 0; s < a.batch; ++s) {
+    const int64_t L = plan_h[kHeaderLen + s * kSeqStride + kSeqLen];
+    max_tn = std::max<int64_t>(max_tn, (L + kBlockN - 1) / kBlockN);
+  }
+  const int64_t gx = max_tn * a.hkv;
+  if (gx > 0x7fffffff || a.batch > 65535) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  if ((int64_t)a.hkv * plan_h[kHeadDim] * 2 * kBlockN > 0x7fffffff)
+    return fail(TILEMIX_EINVAL, "%d KV heads: a 64-row key block spans more than 2 GiB", a.hkv);
+  if (gx == 0) return TILEMIX_OK;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const dim3 grid((unsigned)gx, (unsigned)a.batch);
   if (plan_h[kHeadDim] == 64)
-    hipLaunchKernelGGL(quantize_qk_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(quantize_k_kernel<64>, grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(quantize_qk_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(quantize_k_kernel<128>, grid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "quantize_k launch");
   return TILEMIX_OK;
