@@ -181,8 +181,9 @@ def time_in_pipeline(prep, attend, steps, warmup=20):
 
 def bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, steps):
     """Adaptive routing at the same coverage: the device importance statistic
-    (timed with events), the host ranking and word upload (wall clock), and
-    the prefill under the adaptive words."""
+    (timed with events), the whole routing step with the host ranking and
+    word upload (wall clock) and with the selection on the device (events),
+    and the prefill under the adaptive words."""
     import numpy as np
     import torch
     stream = torch.cuda.current_stream()
@@ -198,13 +199,27 @@ def bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, steps):
     e1.record(stream)
     torch.cuda.synchronize()
     imp_us = e0.elapsed_time(e1) * 1e3 / steps
+    # the whole routing step with the host ranking (wall clock: statistic,
+    # copy, ranking, upload), then with the selection on the device (events:
+    # statistic + selection, nothing leaves the GPU)
     t0 = time.perf_counter()
-    tp.set_routing_adaptive(coverage)
+    tp.set_routing_adaptive(coverage, on_device=False)
     torch.cuda.synchronize()
     route_ms = (time.perf_counter() - t0) * 1e3
+    host_words = tp.words.copy()
+    tp.set_routing_adaptive(coverage)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        tp.set_routing_adaptive(coverage)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    route_dev_us = e0.elapsed_time(e1) * 1e3 / steps
+    if not np.array_equal(tp.words_host(), host_words):
+        raise SystemExit("device-selected adaptive words differ from the host ranking")
     out = torch.empty_like(qd)
     attn_ms = time_in_pipeline(lambda: tp.quantize_k(kd), lambda: tp.attend_qinline(qd, kd, vd, out), steps)
-    P, P8 = legal_pair_counts(cu, tp.words, hq, hkv)
+    P, P8 = legal_pair_counts(cu, tp.words_host(), hq, hkv)
     t_roof = 2 * d * (P - P8) / PEAK_F16 + 2 * d * P / PEAK_F16 + 2 * d * P8 / PEAK_I8
     lens = np.diff(np.asarray(cu, dtype=np.int64))
     tq, tk = sum(-(-int(L) // 128) for L in lens), sum(-(-int(L) // 64) for L in lens)
@@ -214,7 +229,8 @@ def bench_adaptive(tp, qd, kd, vd, cu, hq, hkv, d, coverage, steps):
                                     "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                                     "frac": imp_bytes / (imp_us * 1e-6) / PEAK_HBM,
                                     "algorithmic_bytes": imp_bytes},
-            "route_total_ms": route_ms, "prefill_ms": attn_ms, "frac": t_roof / (attn_ms * 1e-3),
+            "route_total_ms": route_ms, "route_on_device_us": route_dev_us,
+            "prefill_ms": attn_ms, "frac": t_roof / (attn_ms * 1e-3),
             "int8_pair_share": P8 / P}
 
 
@@ -269,7 +285,7 @@ def bench_exposure(coverages=(2500, 5000, 7500), tau=0.5):
         tp.set_routing("sptrans", cov)
         out["sptrans"][str(cov)] = round(exposure(tp.words), 4)
         tp.set_routing_adaptive(cov)
-        out["adaptive"][str(cov)] = round(exposure(tp.words), 4)
+        out["adaptive"][str(cov)] = round(exposure(tp.words_host()), 4)
     return out
 
 

@@ -357,6 +357,27 @@ int tilemix_routing_importance(const int32_t* plan_h, const int32_t* plan_d, con
                                void* workspace, int64_t workspace_bytes, float* importance_d,
                                void* hip_stream);
 
+/* Adaptive routing words selected on the device (same policy and result,
+ * bit for bit, as tilemix_build_routing_adaptive, without the round trip of
+ * the importances through the host) -- [Digest, setup]: the interface
+ * accepts adaptive policies; [Map, "Placement can matter more than the
+ * nominal percentage"].  For each (sequence, KV head) the legal groups are
+ * ordered by (importance, r, G) ascending and the first
+ * N8 = round-half-up(coverage_bp * N_legal / 10000) get bit 1 (INT8); -0
+ * and +0 tie, a NaN importance ranks after +inf (the host builder rejects
+ * NaN instead).  importance_d: device float[Hkv][total_q_tiles][64] from
+ * tilemix_routing_importance (slots of illegal groups ignored); words_d:
+ * device uint64[Hkv][total_q_tiles], every word of every sequence written
+ * (illegal groups' bits 0).  int8_groups_h, legal_groups_h (host, [batch],
+ * may be NULL): N8 and N_legal per sequence, filled once the plan and
+ * coverage are accepted (before the pointer checks and the launch).
+ * One workgroup per (sequence, KV head), enqueued on hip_stream.
+ * Errors: EINVAL for bad plans or coverage, or a missing or misaligned
+ * pointer. */
+int tilemix_select_routing_adaptive(const int32_t* plan_h, const int32_t* plan_d, const float* importance_d,
+                                    int32_t coverage_bp, uint64_t* words_d, int64_t* int8_groups_h,
+                                    int64_t* legal_groups_h, void* hip_stream);
+
 /* ---- Synthetic multi-layer stack ------------------------------------------
  * [Explainer, 数字精度混用到底靠不靠谱]: deeper models pile up more deviation,
  * the error of one layer being carried into the next.  The pages give no

@@ -70,6 +70,7 @@ _SIGNATURES = {
     "tilemix_build_routing_adaptive": ([_P, _I32, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
     "tilemix_importance_workspace_size": ([_P, _P], ctypes.c_int),
     "tilemix_routing_importance": ([_P] * 7 + [_I64, _P, _P], ctypes.c_int),
+    "tilemix_select_routing_adaptive": ([_P, _P, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
     "tilemix_decode_workspace_size": ([_P, _P], ctypes.c_int),
     "tilemix_decode_varlen": ([_P] * 9 + [_I64, _P, _P], ctypes.c_int),
     "tilemix_decode_varlen_noalloc": ([_P] * 10, ctypes.c_int),
@@ -387,6 +388,21 @@ def tilemix_routing_importance(plan_h, plan_d, q_i8, k_i8, q_scale, k_scale, wor
         _stream(stream)))
 
 
+def tilemix_select_routing_adaptive(plan_h, plan_d, importance, coverage_bp: int, words_d, stream=None):
+    """Adaptive words selected on the device into ``words_d`` (int64 tensor
+    holding the uint64 words, [Hkv, total_q_tiles]); returns the per-sequence
+    (int8_groups, legal_groups) counts."""
+    import torch
+    T, B, hq, hkv, d, tq, tk = _dims(plan_h)
+    _sizes(plan_h, plan_d, importance=(importance, hkv * tq * 64), words_d=(words_d, hkv * tq))
+    n8 = np.zeros(max(B, 1), dtype=np.int64)
+    nl = np.zeros(max(B, 1), dtype=np.int64)
+    _check(lib().tilemix_select_routing_adaptive(
+        _hptr(plan_h), _dptr(plan_d, torch.int32, "plan_d"), _dptr(importance, torch.float32, "importance"),
+        int(coverage_bp), _dptr(words_d, torch.int64, "words_d"), _hptr(n8), _hptr(nl), _stream(stream)))
+    return n8[:B], nl[:B]
+
+
 def tilemix_quantize_kv(plan_h, plan_d, k, v, k_i8, v_i8, k_scale, v_scale, stream=None):
     import torch
     T, B, hq, hkv, d, tq, tk = _dims(plan_h)
@@ -508,9 +524,14 @@ class TileMixPrefill:
         w = self.words if self.words.size else np.zeros((1, 1), dtype=np.uint64)
         self.words_d = torch.from_numpy(w.view(np.int64)).to(self.device)
 
-    def set_routing_adaptive(self, coverage_bp: int, stream=None):
+    def set_routing_adaptive(self, coverage_bp: int, stream=None, on_device: bool = True):
         """Content-dependent words from the quantised Q and K of the last
-        ``quantize`` call (device statistic, host ranking, upload)."""
+        ``quantize`` call: the device statistic, then the selection on the
+        device (``words_d`` written in place, nothing crosses to the host;
+        ``words`` is set to None, ``words_host()`` downloads them) and the
+        device importances returned, or with ``on_device=False`` the ranking
+        on the host and an upload (the importances returned as numpy).  Both
+        give the same words, bit for bit."""
         import torch
         if not hasattr(self, "imp_ws"):
             self.imp_ws = torch.empty(max(tilemix_importance_workspace_size(self.plan_h), 16),
@@ -519,12 +540,27 @@ class TileMixPrefill:
                                           device=self.device)
         tilemix_routing_importance(self.plan_h, self.plan_d, self.q_i8, self.k_i8, self.q_scale,
                                    self.k_scale, self.imp_ws, self.importance, stream)
+        if on_device:
+            shape = (self.hkv, max(self.tq, 1))
+            if self.words_d is None or tuple(self.words_d.shape) != shape:
+                self.words_d = torch.zeros(shape, dtype=torch.int64, device=self.device)
+            self.n_int8, self.n_legal = tilemix_select_routing_adaptive(
+                self.plan_h, self.plan_d, self.importance, coverage_bp, self.words_d, stream)
+            self.words = None
+            return self.importance
         imp = self.importance.cpu().numpy()[:, :self.tq]
         self.words, self.g, self.n_int8, self.n_legal = tilemix_build_routing_adaptive(
             self.cu, imp, coverage_bp)
         w = self.words if self.words.size else np.zeros((1, 1), dtype=np.uint64)
         self.words_d = torch.from_numpy(w.view(np.int64)).to(self.device)
         return imp
+
+    def words_host(self):
+        """The routing words in use, [Hkv, total_q_tiles] uint64 on the host
+        (downloads them when they were selected on the device)."""
+        if self.words is None:
+            self.words = self.words_d.cpu().numpy().view(np.uint64)[:, :self.tq].copy()
+        return self.words
 
     def quantize(self, q, k, stream=None):
         tilemix_quantize_qk(self.plan_h, self.plan_d, q, k, self.q_i8, self.k_i8, self.q_scale,

@@ -13,8 +13,9 @@
 //   * Z(kv, r, t) = max over the KV head's query heads;
 //   * importance of group (r, G) = max of Z over its legal tiles minus the max
 //     of Z over the row's legal tiles (binary32).
-// The host ranks the groups of each (sequence, KV head) by (importance, r, G)
-// and routes the first N8 to INT8 (tilemix_build_routing_adaptive).  All
+// The groups of each (sequence, KV head), ranked by (importance, r, G), route
+// their first N8 to INT8: on the device (tilemix_select_routing_adaptive,
+// below) or on the host (tilemix_build_routing_adaptive), bit-identical.  All
 // arithmetic is exact or a fixed sequence of IEEE binary32 operations, so the
 // result is reproducible bit for bit.
 
@@ -182,6 +183,151 @@ int check_ptr(const void* p, const char* name, bool needed) {
   return TILEMIX_OK;
 }
 
+// --------------------------------------------------------------------------
+// Selection of the adaptive words on the device: one workgroup of 1,024
+// threads per (sequence, KV head) routes the N8 least important legal
+// groups to INT8 under the total order (importance, r, G), the order of the
+// host ranking (tilemix_build_routing_adaptive), so the words are the same
+// bit for bit:
+//   * key: the importance as an order-preserving unsigned integer (-0 mapped
+//     to +0 so that equal values tie as a floating-point comparison has
+//     them; NaN after +inf);
+//   * a four-pass radix select, 8 bits a pass from the top, finds the N8-th
+//     smallest key T (an LDS histogram of the candidates' next digit per
+//     pass, one wave scanning it);
+//   * a group is INT8 when its key is below T, or equal to T and among the
+//     first of the equal keys in (r, G) order, as many as N8 still needs;
+//   * the importance layout's slots [row][64] are visited 1,024 at a time in
+//     (r, G) order, so each wave holds one row's 64 groups: the equal keys'
+//     running count is a ballot popcount plus the earlier waves' and rounds'
+//     counts, and the row's word is a ballot.
+// --------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+
+struct SelArgs {
+  const int32_t* plan;
+  const float* imp;  // [Hkv][tq][64]
+  uint64_t* words;   // [Hkv][tq]
+  int32_t hkv, tq, coverage_bp;
+};
+
+__device__ inline uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  const uint32_t mag = u & 0x7fffffffu;
+  if (mag == 0) return 0x80000000u;              // -0 and +0 alike
+  if (mag > 0x7f800000u) return 0xffffffffu;     // NaN after +inf
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline int last_group_of(int r, int L, int g) {
+  const int last_q = min(r * kBlockM + kBlockM - 1, L - 1);
+  return (last_q / kBlockN) / g;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_words_kernel(SelArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wave_cnt[kSelWaves];
+  __shared__ uint32_t s_bin, s_below_bin, s_nlegal;
+  const int seq = blockIdx.x / a.hkv, kv = blockIdx.x % a.hkv;
+  const int32_t* rec = a.plan + kHeaderLen + seq * kSeqStride;
+  const int L = rec[kSeqLen], g = rec[kSeqG], Tm = rec[kSeqTm], qt = rec[kSeqQtOff];
+  if (Tm == 0) return;  // the whole workgroup, before any barrier
+  const float* imp = a.imp + ((size_t)kv * a.tq + qt) * kWordBits;
+  uint64_t* words = a.words + (size_t)kv * a.tq + qt;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rounds = (Tm + kSelWaves - 1) / kSelWaves;  // a wave per row each round
+
+  // legal groups of the sequence and the INT8 count
+  if (tid == 0) s_nlegal = 0;
+  __syncthreads();
+  {
+    uint32_t n = 0;
+    for (int r = tid; r < Tm; r += kSelThreads) n += (uint32_t)last_group_of(r, L, g) + 1;
+    if (n) atomicAdd(&s_nlegal, n);
+  }
+  __syncthreads();
+  const int64_t n_legal = s_nlegal;
+  const int64_t n8 = ((int64_t)a.coverage_bp * n_legal + 5000) / 10000;
+  if (n8 == 0) {
+    for (int r = tid; r < Tm; r += kSelThreads) words[r] = 0ull;
+    return;
+  }
+
+  // radix select of the n8-th smallest key
+  uint32_t prefix = 0, mask = 0;
+  int64_t rank = n8 - 1;  // index of the wanted key among the candidates
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int k = 0; k < rounds; ++k) {
+      const int r = k * kSelWaves + w;
+      if (r < Tm && lane <= last_group_of(r, L, g)) {
+        const uint32_t key = order_key(imp[(size_t)r * kWordBits + lane]);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      // lane l holds bins 4l .. 4l + 3; exclusive scan over the lanes
+      uint32_t c[4], tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = hist[4 * lane + i];
+        tot += c[i];
+      }
+      uint32_t incl = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      uint32_t before = incl - tot;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if ((int64_t)before <= rank && rank < (int64_t)before + c[i]) {
+          s_bin = 4 * lane + i;
+          s_below_bin = before;
+        }
+        before += c[i];
+      }
+    }
+    __syncthreads();
+    prefix |= s_bin << shift;
+    mask |= 255u << shift;
+    rank -= s_below_bin;
+    __syncthreads();  // s_bin is rewritten by the next pass
+  }
+  const uint32_t T = prefix;
+  const int64_t need_eq = rank + 1;  // equal keys still routed, in (r, G) order
+
+  // words: one row per wave per round
+  int64_t carry = 0;
+  for (int k = 0; k < rounds; ++k) {
+    const int r = k * kSelWaves + w;
+    const bool valid = r < Tm && lane <= last_group_of(r, L, g);
+    const uint32_t key = valid ? order_key(imp[(size_t)r * kWordBits + lane]) : 0u;
+    const bool lt = valid && key < T, eq = valid && key == T;
+    const uint64_t be = __ballot(eq);
+    if (lane == 0) wave_cnt[w] = (uint32_t)__popcll(be);
+    __syncthreads();
+    uint32_t wave_off = 0, round_tot = 0;
+#pragma unroll
+    for (int u = 0; u < kSelWaves; ++u) {
+      const uint32_t cu = wave_cnt[u];
+      if (u < w) wave_off += cu;
+      round_tot += cu;
+    }
+    const int64_t eq_idx = carry + wave_off + __popcll(be & ((1ull << lane) - 1ull));
+    const bool int8 = lt || (eq && eq_idx < need_eq);
+    const uint64_t word = __ballot(int8);
+    if (lane == 0 && r < Tm) words[r] = word;
+    carry += round_tot;
+    __syncthreads();  // wave_cnt is rewritten next round
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -247,6 +393,45 @@ int tilemix_routing_importance(const int32_t* plan_h, const int32_t* plan_d, con
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TILEMIX_EHIP, "importance launch: %s", hipGetErrorString(e));
+  return TILEMIX_OK;
+}
+
+int tilemix_select_routing_adaptive(const int32_t* plan_h, const int32_t* plan_d, const float* importance_d,
+                                    int32_t coverage_bp, uint64_t* words_d, int64_t* int8_groups_h,
+                                    int64_t* legal_groups_h, void* hip_stream) {
+  clear_error();
+  int rc = check_plans(plan_h, plan_d);
+  if (rc) return rc;
+  if (coverage_bp < 0 || coverage_bp > 10000)
+    return fail(TILEMIX_EINVAL, "coverage_bp must be in [0, 10000] (got %d)", coverage_bp);
+  const int32_t batch = plan_h[kBatch], hkv = plan_h[kHkv];
+  // the counts, from the plan's geometry (the kernel derives the same)
+  for (int32_t s = 0; s < batch; ++s) {
+    const int32_t* rec = plan_h + kHeaderLen + s * kSeqStride;
+    const int64_t L = rec[kSeqLen], g = rec[kSeqG], Tm = rec[kSeqTm];
+    int64_t n = 0;
+    for (int64_t r = 0; r < Tm; ++r) n += (std::min(r * kBlockM + kBlockM - 1, L - 1) / kBlockN) / g + 1;
+    if (legal_groups_h) legal_groups_h[s] = n;
+    if (int8_groups_h) int8_groups_h[s] = (coverage_bp * n + 5000) / 10000;
+  }
+  const bool any = plan_h[kTotalQTiles] > 0;
+  if ((rc = check_ptr(plan_d, "plan_d", true)) || (rc = check_ptr(importance_d, "importance_d", any)) ||
+      (rc = check_ptr(words_d, "words_d", any)))
+    return rc;
+  if (!any) return TILEMIX_OK;
+  const int64_t blocks = (int64_t)batch * hkv;
+  if (blocks > 0x7fffffff) return fail(TILEMIX_EINVAL, "batch too large for one launch");
+  SelArgs a;
+  a.plan = plan_d;
+  a.imp = importance_d;
+  a.words = words_d;
+  a.hkv = hkv;
+  a.tq = plan_h[kTotalQTiles];
+  a.coverage_bp = coverage_bp;
+  hipLaunchKernelGGL(select_words_kernel, dim3((unsigned)blocks), dim3(kSelThreads), 0,
+                     static_cast<hipStream_t>(hip_stream), a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TILEMIX_EHIP, "word selection launch: %s", hipGetErrorString(e));
   return TILEMIX_OK;
 }
 

@@ -377,3 +377,39 @@ def test_plan_checksum_refuses_a_modified_host_plan():
     bad[9] -= 1                       # work-unit count no longer matches the body
     rc = tm.lib().tilemix_quantize_k(bad.ctypes.data_as(ctypes.c_void_p), fake, fake, fake, fake, None)
     assert rc == -1
+
+
+def test_select_routing_adaptive_validation_and_counts():
+    """The device word selection's argument checks (no launch) and its
+    host-side counts, which equal the oracle's N8 and N_legal."""
+    lens = [300, 0, 129, 4160]
+    cu = synth.cu_seqlens_of(lens)
+    plan = tm.tilemix_build_plan(cu, 2, 2, 64)
+    lib = tm.lib()
+    lib.tilemix_select_routing_adaptive.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_void_p, ctypes.c_void_p]
+    p = ctypes.c_void_p(plan.ctypes.data)
+    fake = ctypes.c_void_p(16)
+    assert lib.tilemix_select_routing_adaptive(p, fake, fake, 10001, fake, None, None, None) == -1
+    assert "coverage_bp" in tm.tilemix_last_error()
+    assert lib.tilemix_select_routing_adaptive(p, fake, fake, 5000, None, None, None, None) == -1
+    assert "words_d" in tm.tilemix_last_error()
+    assert lib.tilemix_select_routing_adaptive(p, fake, ctypes.c_void_p(20), 5000, fake, None, None, None) == -1
+    assert "aligned" in tm.tilemix_last_error()
+    # an empty batch: counts only, nothing launched
+    empty = tm.tilemix_build_plan(synth.cu_seqlens_of([0, 0]), 2, 2, 64)
+    n8 = np.full(2, -1, dtype=np.int64)
+    nl = np.full(2, -1, dtype=np.int64)
+    assert lib.tilemix_select_routing_adaptive(ctypes.c_void_p(empty.ctypes.data), fake, None, 5000, None,
+                                               ctypes.c_void_p(n8.ctypes.data),
+                                               ctypes.c_void_p(nl.ctypes.data), None) == 0
+    assert list(n8) == [0, 0] and list(nl) == [0, 0]
+    for cov in (0, 1, 2500, 7777, 10000):
+        _, _, on8, onl = oracle.routing_words(lens, 2, "band", cov, 0)
+        n8 = np.zeros(len(lens), dtype=np.int64)
+        nl = np.zeros(len(lens), dtype=np.int64)
+        # counts are filled before the pointer checks (words_d NULL: refused)
+        assert lib.tilemix_select_routing_adaptive(p, fake, fake, cov, None, ctypes.c_void_p(n8.ctypes.data),
+                                                   ctypes.c_void_p(nl.ctypes.data), None) == -1
+        assert list(nl) == list(onl) and list(n8) == list(on8)
