@@ -220,9 +220,9 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
 
-  // Every load of the workgroup is issued up front, branch-free (addresses of
-  // keys past the sequence end are clamped to its last key: their scores are
-  // masked and their P is 0), in the order of first use -- the scalars, the
+  // Every load of the workgroup is issued up front, branch-free (the scale
+  // and query indices clamped into range, the key and value rows through the
+  // buffer resources below), in the order of first use -- the scalars, the
   // queries, the wave's key tile, then this thread's share of the values --
   // so the waits before the scores and before P.V each cover only what they
   // need, and the values stream in while the scores are computed.
