@@ -41,7 +41,12 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;            // 4 waves of 64
 constexpr int kChunk = 4 * kBlockN;      // keys per workgroup: one key tile per wave
-constexpr int kMaxG = 8;                 // query heads per workgroup
+// Query heads per workgroup: larger GQA groups split into groups of 4 (the
+// last may be smaller), whose workgroups read the same cache rows (the
+// second read mostly from cache): four heads fit four workgroups per CU,
+// where eight took 190 registers and two per CU (28/4-head varlen step
+// 51.3 -> 49.4 us, the output bit-identical).
+constexpr int kMaxG = 4;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // --------------------------------------------------------------------------
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(KvQuantArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// Partial step: one workgroup per (KV head and group of up to 8 query heads,
+// Partial step: one workgroup per (KV head and group of up to 4 query heads,
 // 256-key chunk, sequence), the KV head fastest in the launch order so that
 // workgroups running side by side read neighbouring bytes of the same cache
 // rows.  Wave w scores key tile 4 c + w; the chunk's softmax state (m, l,
@@ -207,7 +212,7 @@ __device__ inline void i8x4_to_half(uint32_t w, half2v& lo, half2v& hi) {
 // fewer than kMaxG of them (kG = kMaxG: a runtime count, the last group of a
 // larger set may be partial).
 template <int D, int kG>
-__global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void decode_partial_kernel(DecodeArgs a) {
   __shared__ Smem<D> sm;
   const int kv = blockIdx.x / a.head_groups, hg = blockIdx.x % a.head_groups;
   const int chunk = blockIdx.y, seq = blockIdx.z;
@@ -246,9 +251,10 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
   const float s_vp_raw = a.vs[(size_t)kv * a.tk + kt_off + min(vt, (L - 1) / kBlockN)];
   const float s_k_raw = a.ks[(size_t)kv * a.tk + kt_off + min(t, (L - 1) / kBlockN)];
   const uint64_t word = a.words[(size_t)kv * a.tq + rec[kSeqQtOff] + (L - 1) / kBlockM];
-  _Float16 qv[2][D / 64];                   // heads w and w + 4 of the group
+  constexpr int kQPerWave = (kMaxG + 3) / 4;  // query heads each wave quantises
+  _Float16 qv[kQPerWave][D / 64];             // heads w, w + 4, ... of the group
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < kQPerWave; ++u)
 #pragma unroll
     for (int i = 0; i < D / 64; ++i)
       qv[u][i] = a.q[((size_t)seq * a.hq + h0 + min(w + 4 * u, G - 1)) * D + lane + 64 * i];
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(kThreads, kG <= 3 ? 4 : 2) void decode_partial_kern
   // Queries of the group: fp16 copy, and the int8 copy with one scale per
   // (sequence, head) -- the quantiser with a block of one row.
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kQPerWave; ++u) {
     const int h = w + 4 * u;
     if (h >= G) break;
     float x[D / 64];
@@ -561,10 +567,6 @@ void launch_partial(int kg, dim3 grid, hipStream_t st, const DecodeArgs& a) {
     case 1: hipLaunchKernelGGL((decode_partial_kernel<D, 1>), grid, dim3(kThreads), 0, st, a); break;
     case 2: hipLaunchKernelGGL((decode_partial_kernel<D, 2>), grid, dim3(kThreads), 0, st, a); break;
     case 3: hipLaunchKernelGGL((decode_partial_kernel<D, 3>), grid, dim3(kThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_partial_kernel<D, 4>), grid, dim3(kThreads), 0, st, a); break;
-    case 5: hipLaunchKernelGGL((decode_partial_kernel<D, 5>), grid, dim3(kThreads), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((decode_partial_kernel<D, 6>), grid, dim3(kThreads), 0, st, a); break;
-    case 7: hipLaunchKernelGGL((decode_partial_kernel<D, 7>), grid, dim3(kThreads), 0, st, a); break;
     default: hipLaunchKernelGGL((decode_partial_kernel<D, kMaxG>), grid, dim3(kThreads), 0, st, a); break;
   }
 }
