@@ -150,3 +150,40 @@ def test_decode_matches_prefill_last_row_on_exact_cache():
     out = tp(qd, kd, vd).cpu().numpy().astype(np.float64)
     last = out[cu[1:] - 1]
     assert np.abs(g["out"].astype(np.float64) - last).max() <= MAX_ABS
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d", [([4096, 3000, 1, 0, 2500, 4000], 6, 2, 128),
+                                           ([1000, 4096, 77], 7, 1, 64)])
+def test_decode_alternating_steps(lens, hq, hkv, d):
+    """Steps alternate between two query sets, through the workspace and the
+    allocation-free entry points (which share the chunk records' memory
+    between calls): every output equals the first output of its set bit for
+    bit (a record left from the step before would carry the other set's
+    values), and both match the oracle."""
+    _log(f"decode alternating steps lens={lens} hq={hq} hkv={hkv} d={d}")
+    q, k, v, cu = synth.make_qkv(lens, hq, hkv, d, outliers=True, seed=51)
+    q2 = synth.make_qkv(lens, hq, hkv, d, outliers=True, seed=52)[0]
+    qa, qb = synth.decode_queries(q, cu), synth.decode_queries(q2, cu)
+    g = run_decode(qa, k, v, cu, hq, hkv, "sptrans", 7500)
+    td = g["td"]
+    ref_a = oracle_decode(qa, k, v, cu, hq, hkv, g["words"])
+    ref_b = oracle_decode(qb, k, v, cu, hq, hkv, g["words"])
+    qd = [torch.from_numpy(qa).cuda(), torch.from_numpy(qb).cuda()]
+    first = [None, None]
+    outs = []
+    for step in range(48):
+        s = step % 2
+        out = torch.full((len(cu) - 1, hq, d), float("nan"), dtype=torch.float16, device="cuda")
+        td.step(qd[s], out, noalloc=(step % 3 == 2))
+        outs.append((s, out))
+    torch.cuda.synchronize()
+    for s, out in outs:
+        o = out.cpu().numpy()
+        if first[s] is None:
+            first[s] = o
+            assert_close(o, ref_a if s == 0 else ref_b)
+        assert np.array_equal(o.view(np.uint16), first[s].view(np.uint16))
+    assert not np.array_equal(first[0], first[1])
+    for i, L in enumerate(lens):
+        if L == 0:
+            assert not first[0][i].any() and not first[1][i].any()
