@@ -21,6 +21,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <type_traits>
 
@@ -804,11 +805,13 @@ struct RowState {
   float16v o[D / 32];
 };
 
-// code: 0 FP16, 1 INT8, 2 FP8 (the FP8 arm exists only with kThree).
+// code: 0 FP16, 1 INT8, 2 FP8 (the FP8 arm exists only with kThree).  With
+// kMasked, `cross` (wave-uniform) says whether some key of the tile lies past
+// some query's diagonal or the sequence end; only then is the mask applied.
 template <int D, bool kMasked, bool kThree>
 __device__ __forceinline__ void tile_step(const char* buf, int code, float f_i8, float f16s, const half8* qf,
                                           const int4v* qb, const int8v* qc, float f_f8, RowState<D>& st,
-                                          int k0, int qi, int L) {
+                                          int k0, int qi, int L, bool cross) {
   const int lane = threadIdx.x & 63, hh = lane >> 5;
   float16v accv[2];
   float f;
@@ -831,16 +834,21 @@ __device__ __forceinline__ void tile_step(const char* buf, int code, float f_i8,
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) accf[kb][i] = accv[kb][i];
-  // Causal / sequence-end mask, independent of the routing bit: masked
-  // entries become -inf here and P = 0 below (even when f = 0).
-  if (kMasked) {
+  // Causal / sequence-end mask, independent of the routing bit: key
+  // k0 + 4 hh + c (c a compile-time offset) is visible to query qi when
+  // c <= min(qi, L - 1) - k0 - 4 hh; the others become -inf here and give
+  // P = 2^-inf = 0 below.  That needs a positive factor: a zero one (a zero
+  // scale product, every score of the tile zero or below the float range) is
+  // replaced by the least normal float, which leaves each visible score's
+  // exponent argument within 2^-100 of -m (exactly -m unless m is near zero).
+  if (kMasked && cross) {
+    const int lim = min(qi, L - 1) - k0 - hh * 4;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-        if (key > qi || key >= L) accf[kb][i] = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) accf[kb][i] = -INFINITY;
+    f = f > 0.f ? f : FLT_MIN;
   }
   // The vector-ALU softmax runs at raised wave priority: the sooner it
   // finishes, the sooner this wave's P.V matrix instructions are ready to
@@ -872,12 +880,8 @@ __device__ __forceinline__ void tile_step(const char* buf, int code, float f_i8,
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(accf[kb][2 * i], f, negm));
-      float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(accf[kb][2 * i + 1], f, negm));
-      if (kMasked) {
-        e0 = accf[kb][2 * i] == -INFINITY ? 0.f : e0;
-        e1 = accf[kb][2 * i + 1] == -INFINITY ? 0.f : e1;
-      }
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(accf[kb][2 * i], f, negm));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(accf[kb][2 * i + 1], f, negm));
       const half2v pk = {(_Float16)e0, (_Float16)e1};
       psum = __builtin_amdgcn_fdot2(pk, (half2v){(_Float16)1.0f, (_Float16)1.0f}, psum, false);
       pw[kb][i] = __builtin_bit_cast(uint32_t, pk);
@@ -1069,12 +1073,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     grp = ngrp;
     const float f_i8 = (sq * sks[t & (T::kScales - 1)]) * inv_sqrt_d * kLog2e;
     const float f_f8 = kThree ? (sqf * sksf[t & (T::kScales - 1)]) * inv_sqrt_d * kLog2e : 0.f;
-    tile_step<D, decltype(masked)::value, kThree>(buf, code, f_i8, scale16, qf, qb, qc, f_f8, st, t * kBlockN,
-                                                  qi, L);
+    const int k0 = t * kBlockN;
+    if constexpr (!decltype(masked)::value) {
+      tile_step<D, false, kThree>(buf, code, f_i8, scale16, qf, qb, qc, f_f8, st, k0, qi, L, false);
+    } else {
+      // Wave-uniform: a tile none of whose keys any of the wave's queries
+      // sees (or a wave past the sequence end) adds P = 0 and is skipped; a
+      // tile all of whose keys every query of the wave sees skips the mask
+      // (the same code with a branch, not a second copy of the tile step:
+      // two copies in this loop push the kernel past 256 registers).
+      const int qlo = q0 + 32 * w, qhi = min(qlo + 31, L - 1);
+      if (k0 <= qhi && qlo < L) {
+        const bool cross = k0 + kBlockN - 1 > qlo || k0 + kBlockN > L;
+        tile_step<D, true, kThree>(buf, code, f_i8, scale16, qf, qb, qc, f_f8, st, k0, qi, L, cross);
+      }
+    }
   };
   // Tiles t < 2 row lie entirely below the diagonal of every query of the
   // work unit and inside the sequence: no mask.  The rest (the diagonal
-  // tiles and a partial last tile) run in a second loop.
+  // tiles and a partial last tile) run in a second loop, where each wave
+  // takes the mask only on the tiles that cross its own queries' diagonal.
   int t = 0;
   for (; t < 2 * row; ++t) step(t, std::false_type{});
   for (; t <= last_tile; ++t) step(t, std::true_type{});
