@@ -837,10 +837,10 @@ __device__ __forceinline__ void tile_step(const char* buf, int code, float f_i8,
   // Causal / sequence-end mask, independent of the routing bit: key
   // k0 + 4 hh + c (c a compile-time offset) is visible to query qi when
   // c <= min(qi, L - 1) - k0 - 4 hh; the others become -inf here and give
-  // P = 2^-inf = 0 below.  That needs a positive factor: a zero one (a zero
-  // scale product, every score of the tile zero or below the float range) is
-  // replaced by the least normal float, which leaves each visible score's
-  // exponent argument within 2^-100 of -m (exactly -m unless m is near zero).
+  // P = 2^-inf = 0 below.  That needs a positive factor.  The factor is zero
+  // only for an all-zero Q or K block (a nonzero block scale is at least
+  // 2^-24 / 448, so no product of two underflows), whose codes and scores
+  // are all zero: the least normal float in its place leaves them zero.
   if (kMasked && cross) {
     const int lim = min(qi, L - 1) - k0 - hh * 4;
 #pragma unroll

@@ -235,6 +235,15 @@ def test_special_cases_and_determinism():
         cm = np.cumsum(v[a:b].astype(np.float64), axis=0) / np.arange(1, b - a + 1)[:, None, None]
         for h in range(hq):
             assert np.abs(g["out"][a:b, h] - cm[:, h // 2]).max() <= MAX_ABS
+    # an all-zero K block on diagonal tiles: INT8 tiles with a zero scale
+    # product (factor 0) under the causal mask, against the oracle
+    zk = k.copy()
+    zk[64:128] = 0                       # sequence 0, key tile 1 (row 0's diagonal)
+    zk[300 + 128:300 + 192] = 0          # sequence 1, key tile 2 (row 1's diagonal)
+    for cov in (5000, 10000):
+        g = run_gpu(q, zk, v, cu, hq, hkv, "sptrans", cov)
+        assert not np.isnan(g["out"]).any()
+        assert_close(g["out"], oracle.run(q, zk, v, cu, hq, hkv, "sptrans", cov)["out"])
     # 0% is plain attention
     g0 = run_gpu(q, k, v, cu, hq, hkv, "band", 0)
     assert_close(g0["out"], naive_causal_attention(q, k, v, cu, hq, hkv))
