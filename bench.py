@@ -698,9 +698,11 @@ def cpu_baseline(q, k, v, cu, spec, template, coverage, budget_s=20.0, full_head
         full[name] = {"seconds": round(dt, 3), "tokens_per_s": int(cs_[-1]) / dt}
     if full_headline:
         # the headline workload's whole oracle, unsampled (minutes of CPU time)
+        print("cpu_baseline: the whole headline oracle, unsampled ...", file=sys.stderr, flush=True)
         t1 = time.perf_counter()
         oracle.run(q, k, v, cu, spec["hq"], spec["hkv"], template, coverage)
         dt = time.perf_counter() - t1
+        print(f"cpu_baseline: whole headline oracle {dt:.1f} s", file=sys.stderr, flush=True)
         full[spec.get("name", "headline")] = {"seconds": round(dt, 3), "tokens_per_s": tokens / dt}
     cpus, model = _cpu_info()
     # numpy's BLAS pool runs the oracle's matrix products; the rest is one thread
