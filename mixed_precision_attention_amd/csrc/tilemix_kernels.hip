@@ -1014,6 +1014,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       qc[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
+  // The row's key-tile scales go through LDS (1024 tiles per chunk): a scalar
+  // load per tile would make every later lgkmcnt wait include its memory
+  // latency.  The first chunk's (and Q's scales, when they come from the
+  // quantiser) are loaded here, with Q's values, and stored below: staged
+  // after the Q block they had cost each work unit one more memory latency.
+  const float* kscale = a.ks + (size_t)kv * a.tk + kt_off;
+  float* sks = reinterpret_cast<float*>(smem + 2 * T::kBuf);
+  const float* kscalef = kThree ? a.ksf8 + (size_t)kv * a.tk + kt_off : nullptr;
+  float* sksf = sks + T::kScales;  // (FP8 scales, three-path kernel only)
+  constexpr int kPre = T::kScales / kThreads;
+  const int npre = min(T::kScales, last_tile + 1);
+  float scp[kPre], scfp[kThree ? kPre : 1];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int i = tid + j * kThreads;
+    if (i < npre) {
+      scp[j] = kscale[i];
+      if (kThree) scfp[j] = kscalef[i];
+    }
+  }
+  const float sq_ld = kQInline ? 0.f : load_uniform(a.qs + (size_t)head * a.tq + qt_off + row);
+  const float sqf_ld = (kQInline || !kThree) ? 0.f : load_uniform(a.qsf8 + (size_t)head * a.tq + qt_off + row);
   // Let the compiler see the query loads complete here: it does not count the
   // asm-issued tile loads, so a wait it placed later for these would also
   // wait for every tile load in flight.
@@ -1031,25 +1053,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       sqf = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sf)));
     }
   } else {
-    sq = load_uniform(a.qs + (size_t)head * a.tq + qt_off + row);
-    if (kThree) sqf = load_uniform(a.qsf8 + (size_t)head * a.tq + qt_off + row);
+    sq = sq_ld;
+    sqf = sqf_ld;
   }
   const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
   const float scale16 = inv_sqrt_d * kLog2e;
-  // The row's key-tile scales go through LDS (1024 tiles per chunk): a scalar
-  // load per tile would make every later lgkmcnt wait include its memory
-  // latency.
-  const float* kscale = a.ks + (size_t)kv * a.tk + kt_off;
-  float* sks = reinterpret_cast<float*>(smem + 2 * T::kBuf);
-  const float* kscalef = kThree ? a.ksf8 + (size_t)kv * a.tk + kt_off : nullptr;
-  float* sksf = sks + T::kScales;  // (FP8 scales, three-path kernel only)
+  // later chunks (rows of more than 1024 key tiles)
   auto stage_scales = [&](int t0) {
     const int n = min(T::kScales, last_tile + 1 - t0);
     for (int i = tid; i < n; i += kThreads) sks[i] = kscale[t0 + i];
     if (kThree)
       for (int i = tid; i < n; i += kThreads) sksf[i] = kscalef[t0 + i];
   };
-  stage_scales(0);
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int i = tid + j * kThreads;
+    if (i < npre) {
+      sks[i] = scp[j];
+      if (kThree) sksf[i] = scfp[j];
+    }
+  }
 
   RowState<D> st;
   st.m = -INFINITY;
